@@ -1,0 +1,13 @@
+"""PACE periodic / channel-aligned 4-bit recurrent-state decode and chunked prefill for
+AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library libpace.so (C ABI in include/pace.h); this package
+is its thin Python binding plus configuration presets.  PyTorch supplies device memory
+and streams only.
+"""
+from ._lib import (  # noqa: F401
+    LIB, LIB_PATH, EXPORTS, LayerConfig, PaceError, layout, head_alloc, decode_step,
+    flush_requant, prefill_chunk, prefill_workspace_bytes, bf16_decode_step,
+    PACE_OK, PACE_EINVAL, PACE_EUNSUPPORTED, PACE_EHIP,
+)
+from .presets import pace4, pace48, tiny_ref  # noqa: F401

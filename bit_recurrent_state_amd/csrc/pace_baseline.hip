@@ -1,0 +1,99 @@
+// Per-token bf16-state gated-delta decode: the comparator of the PACE throughput study
+// (PACE summary, onedev.kr "Assumptions and limits": periodic INT4 decode is timed
+// against per-token bf16 decode, which reads and writes the bf16 state every token).
+//
+// State layout: bf16 [B][Hv][dv][dk], value-column-major.  One workgroup (4 waves) per
+// (sequence, head); D/8 lanes share a column, each holding 8 consecutive keys, so every
+// wave instruction moves contiguous 1 KB.  Per token:
+//   u = beta (v - a S^T k);  S' = a S + k u^T;  o = S'^T q;  S <- bf16_rne(S').
+#include <hip/hip_runtime.h>
+
+#include "pace_internal.h"
+#include "pace_numerics.h"
+
+namespace pace {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int LPC>
+__device__ inline float seg_sum(float x) {
+#pragma unroll
+  for (int o = LPC / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+template <int D, int IO>
+__global__ __launch_bounds__(kThreads) void bf16_decode_kernel(Bf16Params p) {
+  constexpr int LPC = D / 8;                 // lanes per column
+  constexpr int CPW = 64 / LPC;              // columns per wave per pass
+  constexpr int CPB = CPW * (kThreads / 64); // columns per workgroup per pass
+  constexpr int PASSES = D / CPB;
+  constexpr bool kBf16 = IO == 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x / p.Hv, h = blockIdx.x % p.Hv, kh = h / p.gamma;
+  const int m = lane % LPC;                  // keys 8m .. 8m+7
+  float kk[8], qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const size_t i = ((size_t)b * p.Hk + kh) * D + 8 * m + e;
+    kk[e] = kBf16 ? bf16_to_f32(((const uint16_t*)p.k)[i]) : ((const float*)p.k)[i];
+    qv[e] = kBf16 ? bf16_to_f32(((const uint16_t*)p.q)[i]) : ((const float*)p.q)[i];
+  }
+  const float a = p.a[(size_t)b * p.Hv + h], beta = p.beta[(size_t)b * p.Hv + h];
+  uint16_t* tile = p.state + ((size_t)b * p.Hv + h) * D * D;
+#pragma unroll 2
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int j = pass * CPB + wave * CPW + lane / LPC;
+    uint4* src = (uint4*)(tile + (size_t)j * D + 8 * m);
+    const uint4 raw = *src;
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[2 * e] = bits_f32(w[e] << 16);
+      s[2 * e + 1] = bits_f32(w[e] & 0xFFFF0000u);
+    }
+    float dk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dk += s[e] * kk[e];
+    dk = seg_sum<LPC>(dk);
+    const size_t vi = ((size_t)b * p.Hv + h) * D + j;
+    const float vj = kBf16 ? bf16_to_f32(((const uint16_t*)p.v)[vi]) : ((const float*)p.v)[vi];
+    const float u = beta * (vj - a * dk);
+    float oq = 0.f;
+    uint32_t outw[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s[e] = a * s[e] + kk[e] * u;
+      oq += s[e] * qv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      outw[e] = (uint32_t)f32_to_bf16_rne(s[2 * e]) | ((uint32_t)f32_to_bf16_rne(s[2 * e + 1]) << 16);
+    *src = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    oq = seg_sum<LPC>(oq);
+    if (m == 0) {
+      if (kBf16) ((uint16_t*)p.o)[vi] = f32_to_bf16_rne(oq);
+      else ((float*)p.o)[vi] = oq;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bf16_decode(const Bf16Params& p, int dk, int dv, int io_bf16,
+                              hipStream_t stream) {
+  (void)dv;
+  const unsigned grid = (unsigned)p.B * (unsigned)p.Hv;
+  if (dk == 128) {
+    if (io_bf16) hipLaunchKernelGGL((bf16_decode_kernel<128, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((bf16_decode_kernel<128, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else {
+    if (io_bf16) hipLaunchKernelGGL((bf16_decode_kernel<64, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((bf16_decode_kernel<64, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pace

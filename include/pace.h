@@ -82,7 +82,8 @@
  * DECODE BUFFER LAYOUT (pace_layout_info.buffer_bytes per layer), regions in this
  * order, each padded to 256 bytes:
  *     count : int32 [B][Hv]   tokens buffered since the last rounding (0 .. dP-1 between
- *                             calls).  All heads of one sequence advance together.
+ *                             calls; other values are read as clamped to that range).
+ *                             All heads of one sequence advance together.
  *   buf_kind PACE_BUF_INT8 ([p1] "How it works": uniform configuration, 8-bit keys and
  *   values):
  *     kc    : int8   [B][Hk][dP][dk]  key codes, two's complement, |c| <= 127

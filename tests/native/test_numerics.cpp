@@ -1,0 +1,89 @@
+// Host-side check of the quantiser's scalar numerics (bit_recurrent_state_amd/csrc/
+// pace_numerics.h) against exact long-double arithmetic.  Built and run by
+// tests/test_native_numerics.py; prints "OK <count>" on success.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+
+#include "../../bit_recurrent_state_amd/csrc/pace_numerics.h"
+
+using namespace pace;
+
+static int fails = 0;
+#define EXPECT(c, ...) do { if (!(c)) { if (fails++ < 20) { printf("FAIL line %d: ", __LINE__); printf(__VA_ARGS__); printf("\n"); } } } while (0)
+
+// Smallest bf16 >= d by enumeration of the 8 significant bits.
+static float ref_bf16_ceil(double d) {
+  if (!(d > 0)) return 0.f;
+  int e;
+  double m = std::frexp(d, &e);          // d = m 2^e, 0.5 <= m < 1
+  double r = std::ceil(std::ldexp(m, 8));
+  double v = std::ldexp(r, e - 8);
+  if (d < std::ldexp(1.0, -126)) v = std::ceil(d / std::ldexp(1.0, -133)) * std::ldexp(1.0, -133);
+  return (float)v;
+}
+
+// round-half-even of the exact quotient x / s.
+static double ref_rne_quot(float x, float s) {
+  long double q = (long double)x / (long double)s;
+  long double f = std::floor(q);
+  long double d = q - f;
+  if (d > 0.5L) return (double)(f + 1);
+  if (d < 0.5L) return (double)f;
+  return std::fmod((double)f, 2.0) == 0.0 ? (double)f : (double)(f + 1);
+}
+
+int main() {
+  std::mt19937_64 rng(7);
+  std::uniform_real_distribution<double> U(-1.0, 1.0);
+  long n = 0;
+  // bf16 ceiling from double
+  for (int i = 0; i < 200000; ++i) {
+    double d = std::exp(U(rng) * 60.0);
+    float got = bf16_ceil_from_f64(d), want = ref_bf16_ceil(d);
+    EXPECT(got == want, "bf16_ceil(%.17g) = %.9g want %.9g", d, got, want);
+    // values exactly on a bf16 grid point stay there
+    double on = (double)want;
+    EXPECT(bf16_ceil_from_f64(on) == want, "bf16_ceil on grid %.9g", want);
+    n += 2;
+  }
+  // exact RNE quotient, including constructed exact ties and near ties
+  for (int i = 0; i < 400000; ++i) {
+    float s = ref_bf16_ceil(std::exp(U(rng) * 10.0));
+    float x;
+    const int kind = i % 4;
+    if (kind == 0) {
+      x = (float)(U(rng) * 8.0 * s);
+    } else if (kind == 1) {                     // exact half-integer multiples
+      int k = (int)std::floor(U(rng) * 128);
+      x = (float)((k + 0.5) * (double)s);
+    } else if (kind == 2) {                     // one fp32 ulp either side of a tie
+      int k = (int)std::floor(U(rng) * 128);
+      float t = (float)((k + 0.5) * (double)s);
+      x = std::nextafter(t, (i & 8) ? INFINITY : -INFINITY);
+    } else {
+      x = (float)(U(rng) * 130.0 * s);
+    }
+    float r = 1.0f / s;
+    double got = rne_quotient(x, s, r), want = ref_rne_quot(x, s);
+    EXPECT(got == want, "rne(%.9g / %.9g) = %g want %g", x, s, got, want);
+    n++;
+  }
+  // bf16 round-to-nearest-even of fp32
+  for (int i = 0; i < 100000; ++i) {
+    float x = (float)(U(rng) * std::exp(U(rng) * 20));
+    uint16_t b = f32_to_bf16_rne(x);
+    double v = bf16_to_f32(b);
+    double lo = bf16_to_f32((uint16_t)(b - 1)), hi = bf16_to_f32((uint16_t)(b + 1));
+    EXPECT(std::fabs(v - x) <= std::fabs(lo - x) && std::fabs(v - x) <= std::fabs(hi - x),
+           "bf16 rne of %.9g", x);
+    n++;
+  }
+  if (fails) {
+    printf("FAILED %d\n", fails);
+    return 1;
+  }
+  printf("OK %ld\n", n);
+  return 0;
+}

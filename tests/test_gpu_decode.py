@@ -1,0 +1,222 @@
+"""GPU parity of pace_decode_step / pace_flush_requant / pace_bf16_decode_step against the
+fp64 oracle, called through the C ABI on identical seeded inputs.
+
+Every case starts both sides from the same packed state and decode buffer (seeded random
+fields: any stored code is a legal state) and runs ONE call; the oracle never sees a
+GPU result.  Counts are random per sequence so both the append-only and the flushing
+paths run in every launch."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import pace_oracle as po  # noqa: E402
+from oracle import packing as pk  # noqa: E402
+from pace_synth import make_tokens, random_buffer_parts, random_packed_state_parts  # noqa: E402
+import parity  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import bit_recurrent_state_amd as pace
+    return pace
+
+
+def dev(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def io_dev(x, bf16):
+    return dev(np.asarray(x, dtype=np.float32), torch.bfloat16 if bf16 else torch.float32)
+
+
+def host(t):
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy()
+
+
+CASES = {
+    # name: (B, Hv, Hk, d, group, asym, buf, bf16_io, dP, head_bits)
+    "tiny_sym4_g32_int8": (2, 4, 4, 64, 32, False, "int8", False, 8, None),
+    "pace4_g64_int8": (6, 32, 16, 128, 64, False, "int8", True, 8, None),
+    "pace48_g32_int8": (4, 32, 16, 128, 32, True, "int8", True, 8, "quarter"),
+    "pace48_g32_mixed": (4, 32, 16, 128, 32, True, "mixed", True, 8, "quarter"),
+    "d64_asym_mixed_f32": (3, 8, 4, 64, 32, True, "mixed", False, 5, [8, 4, 4, 8, 4, 4, 4, 8]),
+    "dP1_sym_int8": (2, 4, 2, 128, 32, False, "int8", True, 1, None),
+    "dP16_sym_int8": (2, 4, 2, 64, 32, False, "int8", True, 16, None),
+    "dP32_asym_int8": (2, 4, 2, 64, 32, True, "int8", False, 32, [4, 8, 4, 4]),
+    "sym8_heads": (2, 4, 2, 128, 64, False, "int8", True, 8, [8, 8, 4, 8]),
+}
+
+
+def make_case(name, seed, counts=None):
+    B, Hv, Hk, d, g, asym, buf, bf16, dP, hb = CASES[name]
+    if hb == "quarter":
+        hb = [8 if h % 4 == 1 else 4 for h in range(Hv)]
+    ocfg = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=g, asym=asym, buf=buf, dP=dP,
+                       bf16_io=bf16, head_bits=hb)
+    pace = _lib()
+    gcfg = pace.LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=g, asym=asym, buf=buf,
+                            bf16_io=bf16, dP=dP, head_bits=hb)
+    bits = [ocfg.bits(h) for h in range(Hv)]
+    parts = random_packed_state_parts(seed, B, Hv, d, d, g, bits, asym)
+    state = pk.pack_state(ocfg, pk.state_from_parts(ocfg, parts))
+    if counts is None:
+        rng = np.random.default_rng(seed + 7)
+        counts = rng.integers(0, dP, size=B)
+        counts[0] = dP - 1                    # at least one flushing sequence
+    bufp = random_buffer_parts(seed + 1, B, Hv, Hk, d, d, dP, buf == "mixed", counts=counts)
+    buffer = pk.pack_buffer(ocfg, bufp)
+    toks = make_tokens(seed + 2, B, 1, Hv, Hk, d, d, bf16=bf16)
+    return ocfg, gcfg, state, buffer, toks
+
+
+def run_gpu_decode(gcfg, state, buffer, toks, active=None):
+    pace = _lib()
+    q, k, v, a, beta = toks.token(0)
+    bf16 = gcfg.bf16_io
+    st = dev(state)
+    bu = dev(buffer)
+    o = torch.full((gcfg.B, gcfg.Hv, gcfg.dv), float("nan"),
+                   dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+    act = dev(np.asarray(active, dtype=np.uint8)) if active is not None else None
+    pace.decode_step(gcfg, st, bu, io_dev(q, bf16), io_dev(k, bf16), io_dev(v, bf16), dev(a), dev(beta), o,
+                     active=act)
+    torch.cuda.synchronize()
+    return host(o), st.cpu().numpy(), bu.cpu().numpy()
+
+
+def compare_buffers(ocfg, b_gpu, b_ref, tiles):
+    dg, dr = pk.unpack_buffer(ocfg, b_gpu), pk.unpack_buffer(ocfg, b_ref)
+    assert np.array_equal(dg["count"], dr["count"]), "buffer counts differ"
+    for b, h in tiles:
+        n = int(dr["count"][b, h])
+        kh = h // ocfg.gamma
+        for key in ("a", "beta"):
+            assert np.array_equal(dg[key][b, h, :n], dr[key][b, h, :n]), key
+        assert np.array_equal(dg["kc"][b, kh, :n], dr["kc"][b, kh, :n]), f"k codes (b={b},kh={kh})"
+        assert np.array_equal(dg["ks"][b, kh, :n], dr["ks"][b, kh, :n]), "k scales"
+        if ocfg.buf == "int8":
+            assert np.array_equal(dg["vc"][b, h, :n], dr["vc"][b, h, :n]), "v codes"
+            assert np.array_equal(dg["vs"][b, h, :n], dr["vs"][b, h, :n]), "v scales"
+        else:
+            assert np.array_equal(dg["v"][b, h, :n], dr["v"][b, h, :n]), "bf16 v"
+
+
+def check_states(ocfg, s_gpu, s_in, pre, tiles, label):
+    offs, stride, _ = pk.state_layout(ocfg)
+    qg = pk.unpack_state(ocfg, s_gpu, list(pre.keys()))
+    parity.check_flushed_tiles(pre, qg, label)
+    for b, h in tiles:
+        if (b, h) in pre:
+            continue
+        o = b * stride + offs[h]
+        n = pk.record_parts(ocfg, ocfg.bits(h))[3]
+        assert np.array_equal(s_gpu[o:o + n], s_in[o:o + n]), f"{label} untouched state changed (b={b},h={h})"
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_step_matches_oracle(name):
+    print(f"[decode parity] case={name}", flush=True)
+    ocfg, gcfg, state, buffer, toks = make_case(name, seed=100 + len(name))
+    o_ref, s_ref, b_ref, pre = pk.decode_step_layer(ocfg, state, buffer, *toks.token(0))
+    o_gpu, s_gpu, b_gpu = run_gpu_decode(gcfg, state, buffer, toks)
+    tiles = [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)]
+    parity.check_outputs(o_gpu, o_ref, tiles, name, out_bf16=ocfg.bf16_io)
+    compare_buffers(ocfg, b_gpu, b_ref, tiles)
+    assert len(pre) > 0
+    check_states(ocfg, s_gpu, state, pre, tiles, name)
+
+
+def test_decode_inactive_sequences_untouched():
+    print("[decode parity] active mask", flush=True)
+    ocfg, gcfg, state, buffer, toks = make_case("pace4_g64_int8", seed=7)
+    active = [1, 0, 1, 0, 0, 1]
+    o_ref, s_ref, b_ref, pre = pk.decode_step_layer(ocfg, state, buffer, *toks.token(0), active=active)
+    o_gpu, s_gpu, b_gpu = run_gpu_decode(gcfg, state, buffer, toks, active=active)
+    tiles = [(b, h) for b in range(ocfg.B) if active[b] for h in range(ocfg.Hv)]
+    parity.check_outputs(o_gpu, o_ref, tiles, "active", out_bf16=ocfg.bf16_io)
+    for b in range(ocfg.B):
+        if not active[b]:
+            assert np.isnan(o_gpu[b]).all(), "inactive output written"
+    compare_buffers(ocfg, b_gpu, b_ref, [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)])
+    check_states(ocfg, s_gpu, state, pre, [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)], "active")
+
+
+@pytest.mark.parametrize("name", ["pace4_g64_int8", "pace48_g32_mixed", "d64_asym_mixed_f32"])
+def test_flush_requant_matches_oracle(name):
+    print(f"[flush parity] case={name}", flush=True)
+    ocfg, gcfg, state, buffer, _ = make_case(name, seed=300 + len(name))
+    d = pk.unpack_buffer(ocfg, buffer)
+    mask = np.array([1 if b % 3 != 1 else 0 for b in range(ocfg.B)], dtype=np.uint8)
+    s_ref, b_ref, pre = pk.flush_layer(ocfg, state, buffer, seq_mask=mask)
+    pace = _lib()
+    st, bu = dev(state), dev(buffer)
+    pace.flush_requant(gcfg, st, bu, seq_mask=dev(mask))
+    torch.cuda.synchronize()
+    s_gpu, b_gpu = st.cpu().numpy(), bu.cpu().numpy()
+    dg = pk.unpack_buffer(ocfg, b_gpu)
+    assert np.array_equal(dg["count"], pk.unpack_buffer(ocfg, b_ref)["count"])
+    tiles = [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)]
+    check_states(ocfg, s_gpu, state, pre, tiles, name)
+    assert any(d["count"][b, 0] > 0 and mask[b] for b in range(ocfg.B))
+
+
+def test_decode_zero_state_zero_inputs_gives_zero():
+    """Special case of the recurrence: S = 0 and v = 0 keep everything at zero."""
+    print("[decode parity] zero state", flush=True)
+    ocfg, gcfg, _, _, toks = make_case("pace4_g64_int8", seed=9)
+    pace = _lib()
+    L = pace.layout(gcfg)
+    st = torch.zeros(L["state_bytes"], dtype=torch.uint8, device="cuda")
+    bu = torch.zeros(L["buffer_bytes"], dtype=torch.uint8, device="cuda")
+    q, k, v, a, beta = toks.token(0)
+    o = torch.empty((gcfg.B, gcfg.Hv, gcfg.dv), dtype=torch.bfloat16, device="cuda")
+    for step in range(gcfg.dP):
+        pace.decode_step(gcfg, st, bu, io_dev(q, True), io_dev(k, True), io_dev(0 * v, True), dev(a),
+                         dev(beta), o)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(o.float()).item() == 0
+    d = pk.unpack_buffer(ocfg, bu.cpu().numpy())
+    assert np.all(d["count"] == 0)
+    qs = pk.unpack_state(ocfg, st.cpu().numpy(), [(0, 0), (5, 31)])
+    for b, h in [(0, 0), (5, 31)]:
+        assert np.all(qs[b][h].scales == 0)
+
+
+def _bf16_ref_step(S, q, k, v, a, beta):
+    """Per-token bf16 baseline, fp64: u = beta (v - a S^T k); S' = a S + k u^T; o = S'^T q."""
+    S2, _ = po.exact_step(S, k, v, a, beta)
+    return S2, po.readout(S2, q)
+
+
+@pytest.mark.parametrize("bf16_io,d", [(True, 128), (False, 64)])
+def test_bf16_baseline_matches_oracle(bf16_io, d):
+    print(f"[bf16 baseline parity] d={d}", flush=True)
+    B, Hv, Hk = 3, 8, 4
+    rng = np.random.default_rng(d)
+    S = po.bf16_rne(rng.standard_normal((B, Hv, d, d)) * 0.3)        # [b, h, col, key]
+    toks = make_tokens(d + 1, B, 1, Hv, Hk, d, d, bf16=bf16_io)
+    q, k, v, a, beta = toks.token(0)
+    pace = _lib()
+    cfg = pace.LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=32, bf16_io=bf16_io)
+    st = dev(S.astype(np.float32), torch.bfloat16)
+    o = torch.empty((B, Hv, d), dtype=torch.bfloat16 if bf16_io else torch.float32, device="cuda")
+    pace.bf16_decode_step(cfg, st, io_dev(q, bf16_io), io_dev(k, bf16_io), io_dev(v, bf16_io), dev(a), dev(beta), o)
+    torch.cuda.synchronize()
+    S_gpu = host(st)
+    o_gpu = host(o)
+    for b in range(B):
+        for h in range(Hv):
+            kh = h // (Hv // Hk)
+            S2, oo = _bf16_ref_step(S[b, h].T, q[b, kh], k[b, kh], v[b, h], float(a[b, h]), float(beta[b, h]))
+            assert parity.rel_err_io(o_gpu[b, h], oo, bf16_io) <= parity.TOL_REL
+            # stored state = bf16 rounding of the updated state (one bf16 ulp allowed for
+            # fp32-vs-fp64 differences at rounding boundaries)
+            err = np.abs(S_gpu[b, h].T - S2)
+            assert np.all(err <= np.abs(S2) * 2.0 ** -7 + 1e-6)

@@ -1,0 +1,143 @@
+"""GPU parity of pace_prefill_chunk, and the tiny reference configuration end to end
+(512-token prefill in two 256-token chunks, then 64 decode tokens at dP = 8).
+
+Protocol: the oracle runs its own trajectory; every GPU call starts from the oracle's
+packed state (and buffer), so one legal near-tie code flip cannot cascade.  Multi-chunk
+calls are additionally checked for self-consistency (one call over several chunks equals
+the same chunks issued as separate calls, bit for bit)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import pace_oracle as po  # noqa: E402
+from oracle import packing as pk  # noqa: E402
+from pace_synth import make_tokens  # noqa: E402
+import parity  # noqa: E402
+from test_gpu_decode import dev, io_dev, host  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import bit_recurrent_state_amd as pace
+    return pace
+
+
+PCASES = {
+    # name: (B, Hv, Hk, d, group, asym, bf16, head_bits)
+    "tiny_sym4_g32_f32": (2, 4, 4, 64, 32, False, False, None),
+    "pace4_g64_bf16": (2, 32, 16, 128, 64, False, True, None),
+    "pace48_g32_bf16": (2, 8, 4, 128, 32, True, True, [8, 4, 4, 4, 4, 8, 4, 4]),
+}
+
+
+def cfgs(name, dP=8):
+    B, Hv, Hk, d, g, asym, bf16, hb = PCASES[name]
+    o = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=g, asym=asym, buf="int8", dP=dP,
+                    bf16_io=bf16, head_bits=hb)
+    gc = _lib().LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=g, asym=asym, buf="int8",
+                            bf16_io=bf16, dP=dP, head_bits=hb)
+    return o, gc
+
+
+def gpu_prefill(gcfg, state_bytes, span):
+    pace = _lib()
+    q, k, v, a, beta = span
+    bf16 = gcfg.bf16_io
+    T = a.shape[1]
+    st = dev(state_bytes)
+    o = torch.empty((gcfg.B, T, gcfg.Hv, gcfg.dv), dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+    ws_n = pace.prefill_workspace_bytes(gcfg, T)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda") if ws_n else None
+    pace.prefill_chunk(gcfg, st, io_dev(q, bf16), io_dev(k, bf16), io_dev(v, bf16), dev(a), dev(beta), o,
+                       workspace=ws)
+    torch.cuda.synchronize()
+    return host(o), st.cpu().numpy()
+
+
+def check_prefill_call(ocfg, gcfg, state_in, span, tiles, label):
+    o_ref, s_ref, pre = pk.prefill_layer(ocfg, state_in, *span, tiles=tiles)
+    o_gpu, s_gpu = gpu_prefill(gcfg, state_in, span)
+    T = span[3].shape[1]
+    for b, h in tiles:
+        for t in range(T):
+            e = parity.rel_err_io(o_gpu[b, t, h], o_ref[b, t, h], ocfg.bf16_io)
+            assert e <= parity.TOL_REL, f"{label} o (b={b}, t={t}, h={h}) rel err {e:.3g}"
+    qg = pk.unpack_state(ocfg, s_gpu, tiles)
+    parity.check_flushed_tiles(pre, qg, label)
+    return s_ref
+
+
+@pytest.mark.parametrize("name", list(PCASES))
+def test_prefill_chunks_match_oracle(name):
+    print(f"[prefill parity] case={name}", flush=True)
+    ocfg, gcfg = cfgs(name)
+    toks = make_tokens(40 + len(name), ocfg.B, 356, ocfg.Hv, ocfg.Hk, ocfg.dk, ocfg.dv, bf16=ocfg.bf16_io)
+    tiles = [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)]
+    zero = np.zeros(pk.state_layout(ocfg)[2], dtype=np.uint8)
+    s1 = check_prefill_call(ocfg, gcfg, zero, toks.span(0, 256), tiles, name + "/chunk1")
+    # a partial chunk continuing from the oracle's rounded state
+    check_prefill_call(ocfg, gcfg, s1, toks.span(256, 356), tiles, name + "/partial")
+
+
+def test_prefill_multi_chunk_call_equals_separate_calls():
+    print("[prefill] multi-chunk self-consistency", flush=True)
+    ocfg, gcfg = cfgs("pace48_g32_bf16")
+    toks = make_tokens(77, ocfg.B, 600, ocfg.Hv, ocfg.Hk, ocfg.dk, ocfg.dv, bf16=True)
+    zero = np.zeros(pk.state_layout(ocfg)[2], dtype=np.uint8)
+    o_all, s_all = gpu_prefill(gcfg, zero, toks.span(0, 600))
+    st = zero
+    outs = []
+    for t0, t1 in [(0, 256), (256, 512), (512, 600)]:
+        o, st = gpu_prefill(gcfg, st, toks.span(t0, t1))
+        outs.append(o)
+    assert np.array_equal(s_all, st)
+    assert np.array_equal(o_all, np.concatenate(outs, axis=1))
+
+
+def test_prefill_long_shape_first_chunk_sampled():
+    """Launch configuration of the long-prefill workload (4 sequences, 32 value / 16 key
+    heads, d = 128, bf16), one 256-token chunk; sampled tiles against the oracle."""
+    print("[prefill parity] long shape, sampled tiles", flush=True)
+    B, Hv, Hk, d = 4, 32, 16, 128
+    ocfg = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, asym=False, buf="int8", dP=8, bf16_io=True)
+    gcfg = _lib().LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, bf16_io=True)
+    toks = make_tokens(4, B, 256, Hv, Hk, d, d, bf16=True)
+    zero = np.zeros(pk.state_layout(ocfg)[2], dtype=np.uint8)
+    tiles = [(0, 0), (1, 7), (2, 16), (3, 31)]
+    check_prefill_call(ocfg, gcfg, zero, toks.span(0, 256), tiles, "long/first-chunk")
+
+
+def test_tiny_reference_end_to_end():
+    """Tiny reference: B = 2, 4 heads, d = 64, fp32, sym int4 g = 32, int8 buffer,
+    512-token prompt (2 chunks) then 64 decode tokens (8 flushes).  Every GPU call
+    starts from the oracle's packed state / buffer of that point."""
+    print("[tiny reference] prefill + decode", flush=True)
+    ocfg, gcfg = cfgs("tiny_sym4_g32_f32")
+    T = 512 + 64
+    toks = make_tokens(0, ocfg.B, T, ocfg.Hv, ocfg.Hk, ocfg.dk, ocfg.dv)
+    tiles = [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)]
+    state = np.zeros(pk.state_layout(ocfg)[2], dtype=np.uint8)
+    for c in range(2):
+        state = check_prefill_call(ocfg, gcfg, state, toks.span(256 * c, 256 * (c + 1)), tiles, f"tiny/chunk{c}")
+    buffer = np.zeros(pk.buffer_layout(ocfg)[1], dtype=np.uint8)
+    from test_gpu_decode import run_gpu_decode, compare_buffers, check_states
+
+    class One:
+        def __init__(self, t):
+            self.t = t
+
+        def token(self, _):
+            return toks.token(self.t)
+
+    flushes = 0
+    for t in range(512, T):
+        o_ref, s_ref, b_ref, pre = pk.decode_step_layer(ocfg, state, buffer, *toks.token(t))
+        o_gpu, s_gpu, b_gpu = run_gpu_decode(gcfg, state, buffer, One(t))
+        parity.check_outputs(o_gpu, o_ref, tiles, f"tiny/decode{t}")
+        compare_buffers(ocfg, b_gpu, b_ref, tiles)
+        check_states(ocfg, s_gpu, state, pre, tiles, f"tiny/decode{t}")
+        flushes += bool(pre)
+        state, buffer = s_ref, b_ref
+    assert flushes == 8

@@ -1,0 +1,147 @@
+"""CPU tests of the C ABI library: it loads, exports every symbol include/pace.h
+declares, and its host-only entry points (layout, bit accounting, head allocation,
+argument validation) agree with the oracle.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import pace_oracle as po
+from oracle import packing as pk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pace.h")
+
+
+def _pace():
+    import bit_recurrent_state_amd as pace
+    return pace
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pace_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    pace = _pace()
+    names = declared_functions()
+    assert "pace_decode_step" in names and "pace_prefill_chunk" in names
+    lib = ctypes.CDLL(pace.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pace.h but not exported"
+    assert set(pace.EXPORTS) == set(names)
+
+
+CFGS = [
+    dict(B=64, Hv=32, Hk=16, d=128, g=64, asym=False, buf="int8", dP=8, hb=None),
+    dict(B=64, Hv=32, Hk=16, d=128, g=32, asym=True, buf="int8", dP=8, hb="quarter"),
+    dict(B=64, Hv=32, Hk=16, d=128, g=32, asym=True, buf="mixed", dP=8, hb="quarter"),
+    dict(B=2, Hv=4, Hk=4, d=64, g=32, asym=False, buf="int8", dP=8, hb=None),
+    dict(B=3, Hv=8, Hk=2, d=64, g=32, asym=True, buf="mixed", dP=32, hb=[8, 4, 4, 8, 4, 4, 4, 4]),
+]
+
+
+def _cfgs(c):
+    hb = c["hb"]
+    if hb == "quarter":
+        hb = [8 if h < c["Hv"] // 4 else 4 for h in range(c["Hv"])]
+    pace = _pace()
+    g = pace.LayerConfig(B=c["B"], Hv=c["Hv"], Hk=c["Hk"], dk=c["d"], dv=c["d"], group=c["g"],
+                         asym=c["asym"], buf=c["buf"], dP=c["dP"], head_bits=hb)
+    o = pk.LayerCfg(B=c["B"], Hv=c["Hv"], Hk=c["Hk"], dk=c["d"], dv=c["d"], group=c["g"],
+                    asym=c["asym"], buf=c["buf"], dP=c["dP"], head_bits=hb)
+    return g, o, hb
+
+
+@pytest.mark.parametrize("c", CFGS)
+def test_layout_and_accounting_agree_with_oracle(c):
+    pace = _pace()
+    g, o, hb = _cfgs(c)
+    L = pace.layout(g)
+    _, stride, total = pk.state_layout(o)
+    _, btotal = pk.buffer_layout(o)
+    assert L["state_bytes"] == total and L["seq_stride"] == stride
+    assert L["buffer_bytes"] == btotal
+    bits = hb if hb is not None else [4] * c["Hv"]
+    assert L["payload_bits"] == pytest.approx(po.payload_bits(bits, c["g"], c["asym"]), abs=1e-12)
+    assert L["buffer_bits_model"] == pytest.approx(
+        po.buffer_bits_model(c["d"], c["d"], c["Hv"] // c["Hk"], c["dP"], c["buf"]), abs=1e-12)
+    assert L["buffer_bits_actual"] == pytest.approx(btotal * 8 / (c["B"] * c["Hv"] * c["d"] ** 2))
+
+
+def test_pace48_payload_is_the_printed_value():
+    pace = _pace()
+    g, _, _ = _cfgs(CFGS[1])
+    assert abs(pace.layout(g)["payload_bits"] - 5.66) < 0.005
+
+
+def test_head_alloc_matches_oracle():
+    pace = _pace()
+    rng = np.random.default_rng(0)
+    for trial in range(50):
+        H = int(rng.integers(1, 64))
+        e = rng.uniform(0, 2, H)
+        a = rng.uniform(0.3, 1.0, H)
+        if trial % 5 == 0:
+            a[0] = 1.0                     # no decay: infinite retained error
+        if trial % 3 == 0 and H > 2:
+            e[1], a[1] = e[2], a[2]        # tie
+        n8 = po.quarter(H)
+        bits, E = pace.head_alloc(e, a, 8, n8)
+        rb, rE = po.head_alloc(e, a, 8, n8)
+        assert bits.tolist() == rb.tolist()
+        assert np.allclose(E[np.isfinite(rE)], rE[np.isfinite(rE)], rtol=1e-14)
+        assert np.all(np.isinf(E) == np.isinf(rE))
+
+
+def test_validation_errors():
+    pace = _pace()
+    bad = [
+        dict(B=0), dict(Hk=3), dict(group=48), dict(dP=0),
+    ]
+    for kw in bad:
+        c = pace.LayerConfig(B=2, Hv=4, Hk=4, dk=64, dv=64, group=32)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        with pytest.raises(pace.PaceError) as ei:
+            pace.layout(c)
+        assert ei.value.status == pace.PACE_EINVAL, kw
+    unsupported = [dict(dk=96, dv=96, group=32), dict(dP=33), dict(Hv=128, Hk=128), dict(chunk=128),
+                   dict(dk=128, dv=64)]
+    for kw in unsupported:
+        c = pace.LayerConfig(B=2, Hv=4, Hk=4, dk=64, dv=64, group=32)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        with pytest.raises(pace.PaceError) as ei:
+            pace.layout(c)
+        assert ei.value.status == pace.PACE_EUNSUPPORTED, kw
+    c = pace.LayerConfig(B=2, Hv=4, Hk=4, dk=64, dv=64, group=32, head_bits=[4, 5, 4, 4])
+    with pytest.raises(pace.PaceError):
+        pace.layout(c)
+    with pytest.raises(pace.PaceError):
+        pace.head_alloc([1.0, -1.0], [0.9, 0.9], 8, 1)
+    with pytest.raises(pace.PaceError):
+        pace.head_alloc([1.0, 1.0], [0.9, 0.0], 8, 1)
+
+
+def test_null_pointers_rejected_before_any_launch():
+    pace = _pace()
+    c = pace.LayerConfig(B=2, Hv=4, Hk=4, dk=64, dv=64, group=32)._c()
+    L = pace._lib
+    st = L.LIB.pace_decode_step(ctypes.byref(c), None, None, None, None, None, None, None, None, None, None)
+    assert st == pace.PACE_EINVAL
+    st = L.LIB.pace_flush_requant(ctypes.byref(c), None, None, None, None)
+    assert st == pace.PACE_EINVAL
+    st = L.LIB.pace_prefill_chunk(ctypes.byref(c), None, None, None, None, None, None, 4, None, None, 0, None)
+    assert st == pace.PACE_EINVAL
+    st = L.LIB.pace_bf16_decode_step(ctypes.byref(c), None, None, None, None, None, None, None, None)
+    assert st == pace.PACE_EINVAL
+    # misaligned (fake, never dereferenced) pointers
+    fake = ctypes.c_void_p(0x1001)
+    st = L.LIB.pace_decode_step(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, None, fake, None)
+    assert st == pace.PACE_EINVAL
+    assert L.LIB.pace_status_str(-2).decode().startswith("PACE_EUNSUPPORTED")
