@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""Decode throughput of the PACE periodic int4 state path on one MI355X.
+
+Workload (PACE-4 decode): B = 64 sequences, 32 value heads over 16 key heads, d = 128,
+bf16 q/k/v/o, symmetric int4 state with 64-key channel-aligned groups and bf16 scales,
+int8 decode buffer, dP = 8, a 512-token context, L = 24 independent gated-delta layers
+(the per-step working set, ~505 MB of state + buffer, is twice the 256 MB Infinity
+Cache, so the state stream comes from HBM).  Inputs are seeded synthetic tensors with
+the column-outlier structure (4 of 128 value channels per head scaled x8 on runs of
+50-200 tokens), generated on the device; the 512-token context is written by
+pace_prefill_chunk before timing.
+
+One bench "step" = one decode period: dP tokens x L layers of pace_decode_step, i.e. every
+decode row of the path (append, dequantise, replay, output, fold, requantise) once per
+(layer, head, sequence).  A period is captured once in a HIP graph with an event pair
+around every launch; `--steps` replays are timed.  value = B * dP * steps / time.
+
+roofline: the decode kernel's algorithmic bytes per launch (state read 8704 B, buffered
+tokens read, q/k/v/a/beta in, append write, o out, and on flushing steps the 8704 B state
+write, per (sequence, head)) divided by its mean launch duration from the in-graph events.
+cpu_baseline: the fp64 oracle on a bounded sample of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--layers", type=int, default=24)
+    ap.add_argument("--heads", type=int, default=32)
+    ap.add_argument("--kv-heads", type=int, default=16)
+    ap.add_argument("--dim", type=int, default=128)
+    ap.add_argument("--dP", type=int, default=8)
+    ap.add_argument("--context", type=int, default=512)
+    ap.add_argument("--variant", choices=["pace4", "pace48-int8", "pace48-mixed"], default="pace4")
+    ap.add_argument("--baseline", action="store_true", default=True)
+    ap.add_argument("--no-baseline", dest="baseline", action="store_false")
+    ap.add_argument("--cpu-baseline", action="store_true", default=True)
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--seed", type=int, default=1)
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ inputs ----
+
+def make_layer_inputs(torch, B, T, Hv, Hk, d, seed, t_offset=0, timeline=768):
+    """Seeded synthetic token inputs on the device (same distributions as the
+    pace_synth generator: normalised q/k, N(0,1) v with column outliers,
+    a = exp(-softplus(N(-4,1))), beta = sigmoid(N(0,1)))."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    dev = "cuda"
+    q = torch.randn((B, T, Hk, d), generator=g, device=dev)
+    k = torch.randn((B, T, Hk, d), generator=g, device=dev)
+    v = torch.randn((B, T, Hv, d), generator=g, device=dev)
+    a = torch.exp(-torch.nn.functional.softplus(torch.randn((B, T, Hv), generator=g, device=dev) - 4.0))
+    beta = torch.sigmoid(torch.randn((B, T, Hv), generator=g, device=dev))
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    # column outliers on the token timeline
+    rng = np.random.default_rng(seed)
+    chans = np.stack([rng.choice(d, size=4, replace=False) for _ in range(Hv)])        # [Hv, 4]
+    on = np.zeros((B, Hv, 4, timeline), dtype=bool)
+    for b in range(B):
+        for h in range(Hv):
+            for c in range(4):
+                state = bool(rng.integers(0, 2))
+                t = 0
+                while t < timeline:
+                    run = int(rng.integers(50, 201))
+                    if state:
+                        on[b, h, c, t:t + run] = True
+                    state = not state
+                    t += run
+    on = torch.from_numpy(on[..., t_offset:t_offset + T]).to(dev)                      # [B, Hv, 4, T]
+    gain = torch.where(on, 8.0, 1.0).permute(0, 3, 1, 2)                                # [B, T, Hv, 4]
+    idx = torch.from_numpy(chans).to(dev).view(1, 1, Hv, 4).expand(B, T, Hv, 4)
+    v.scatter_(3, idx, torch.gather(v, 3, idx) * gain)
+    bf = torch.bfloat16
+    return (q.to(bf).contiguous(), k.to(bf).contiguous(), v.to(bf).contiguous(),
+            a.float().contiguous(), beta.float().contiguous())
+
+
+# ------------------------------------------------------------------ timing ----
+
+def algorithmic_bytes_per_launch(cfg, n0, L):
+    """Bytes one pace_decode_step launch must move, per its definition, summed over the
+    B x Hv tiles, for a buffer count n0 before the step.  State read, previous buffered
+    tokens (k codes+scale per key head shared by gamma heads, v codes+scale, a, beta),
+    current q/k/v (bf16) and a/beta, the appended token, o, and the state write on the
+    flushing step."""
+    B, Hv, Hk, d, dP = cfg.B, cfg.Hv, cfg.Hk, cfg.dk, cfg.dP
+    gamma = Hv // Hk
+    rec = L["seq_stride"] / Hv                            # mean record bytes per head
+    if cfg.buf == "int8":
+        tok = d / gamma + 4 / gamma + d + 4 + 4 + 4          # per value head: k(shared) + v + a + beta
+    else:
+        tok = d / 2 / gamma + 4 / gamma + 2 * d + 4 + 4
+    io_in = (2 * d * 2) / gamma + d * 2 + 8                 # q, k (shared per key head), v, a, beta
+    o_out = d * 2
+    flush = (n0 + 1) >= dP
+    per_tile = rec + n0 * tok + io_in + o_out + (rec if flush else tok)
+    return per_tile * B * Hv
+
+
+def kernel_durations(torch, stream, calls, periods=2):
+    """Mean GPU duration of each launch in `calls`, from event pairs recorded around it on
+    its stream.  Returns [periods, len(calls)] in ms."""
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(periods)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(2.4e9 * 0.2))          # ~0.2 s spin while the launches queue up
+        for p in range(periods):
+            for i, c in enumerate(calls):
+                ev[p][i][0].record(stream)
+                c()
+                ev[p][i][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([[s.elapsed_time(e) for s, e in row] for row in ev])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build's path runs on a single MI355X and "
+              f"has no multi-GPU mode (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_recurrent_state_amd as pace
+
+    torch.cuda.set_device(0)
+    B, Hv, Hk, d, dP, Lyr = args.batch, args.heads, args.kv_heads, args.dim, args.dP, args.layers
+    if args.variant == "pace4":
+        cfg = pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP)
+    else:
+        # head map: a quarter of the heads at 8 bits (fixed map; the E_h ranking itself is
+        # exercised by pace_head_alloc in the tests)
+        hb = [8 if h % 4 == 0 else 4 for h in range(Hv)]
+        cfg = pace.pace48(hb, B=B, Hv=Hv, Hk=Hk, d=d, dP=dP, buf="int8" if args.variant == "pace48-int8" else "mixed")
+    L = pace.layout(cfg)
+    log(f"variant {args.variant} B={B} Hv={Hv} Hk={Hk} d={d} dP={dP} layers={Lyr} "
+        f"state/layer {L['state_bytes'] / 1e6:.1f} MB buffer/layer {L['buffer_bytes'] / 1e6:.1f} MB")
+
+    # ---- per-layer state, buffer, decode inputs; 512-token context by prefill
+    layers = []
+    t0 = time.time()
+    for l in range(Lyr):
+        st = torch.zeros(L["state_bytes"], dtype=torch.uint8, device="cuda")
+        bu = torch.zeros(L["buffer_bytes"], dtype=torch.uint8, device="cuda")
+        seed = 1000 * args.seed + l
+        ctx = make_layer_inputs(torch, B, args.context + dP, Hv, Hk, d, seed)
+        o_ctx = torch.empty((B, args.context, Hv, d), dtype=torch.bfloat16, device="cuda")
+        pq, pk_, pv, pa, pb = (x[:, :args.context].contiguous() for x in ctx)
+        ws_n = pace.prefill_workspace_bytes(cfg, args.context)
+        ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
+        pace.prefill_chunk(cfg, st, pq, pk_, pv, pa, pb, o_ctx, workspace=ws)
+        toks = [tuple(x[:, args.context + t].contiguous() for x in ctx) for t in range(dP)]
+        o = torch.empty((B, Hv, d), dtype=torch.bfloat16, device="cuda")
+        layers.append(dict(state=st, buf=bu, toks=toks, o=o))
+        del ctx, o_ctx, pq, pk_, pv, pa, pb, ws
+    torch.cuda.synchronize()
+    log(f"context prefilled in {time.time() - t0:.1f}s")
+
+    # ---- one decode period (dP tokens x L layers) as pre-marshalled calls
+    stream = torch.cuda.Stream()
+    calls = []
+    for t in range(dP):
+        for ly in layers:
+            q, k, v, a, b_ = ly["toks"][t]
+            calls.append(pace.prepare_decode_step(cfg, ly["state"], ly["buf"], q, k, v, a, b_, ly["o"], stream=stream))
+    n_launch = len(calls)
+    with torch.cuda.stream(stream):
+        for c in calls:                      # warm the path once outside capture
+            c()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for c in calls:
+            c()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+
+    # timed region: graph replays
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = B * dP * args.steps / (total_ms / 1e3)
+
+    # per-launch kernel durations: the same period launched eagerly on the same stream,
+    # each launch between two events; every launch is enqueued behind a GPU spin first,
+    # so the brackets hold GPU work only
+    kern_ms = kernel_durations(torch, stream, calls, periods=2)
+    # roofline of the decode kernel: algorithmic bytes / mean launch duration
+    per_pos = np.array([algorithmic_bytes_per_launch(cfg, t, L) for t in range(dP)])
+    bytes_per_launch = float(per_pos.mean())
+    kern_ms = kern_ms.mean(axis=0)
+    mean_kern_s = float(kern_ms.mean()) / 1e3
+    achieved = bytes_per_launch / mean_kern_s / 1e9
+    stream_gbs = bytes_per_launch * n_launch * args.steps / (total_ms / 1e3) / 1e9
+    log(f"decode: {tokens_per_s:,.0f} tok/s, {ms_per_step:.3f} ms/period, kernel mean {kern_ms.mean() * 1e3:.2f} us "
+        f"(flush step {kern_ms.reshape(dP, Lyr)[-1].mean() * 1e3:.2f} us), {achieved:.0f} GB/s in-kernel, "
+        f"{stream_gbs:.0f} GB/s over the timed region")
+
+    result = {
+        "metric": "decode tokens/s & achieved HBM GB/s (% peak), int4 state dP=8, B=1..128",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 state / int8 buffer / bf16 io, fp32 + int32 accumulate",
+        "data": "synthetic (seeded; column-outlier value channels)",
+        "config": {"workload": f"{args.variant} decode, {Lyr} gated-delta layers x {Hv} value heads "
+                               f"({Hk} key heads), d={d}, B={B}, dP={dP}, {args.context}-token context; "
+                               f"step = one decode period ({dP} tokens x {Lyr} layers)",
+                   "global_batch": B, "seq_len": args.context, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<128,1,0,1>", "bytes_per_launch": round(bytes_per_launch),
+                     "mean_launch_us": round(kern_ms.mean() * 1e3, 3),
+                     "timed_region_GBps": round(stream_gbs, 1)},
+    }
+
+    # ---- bf16 per-token-state baseline on the same shape
+    if args.baseline:
+        try:
+            result["bf16_baseline"] = run_bf16_baseline(torch, pace, args, cfg, layers)
+        except Exception as e:  # noqa: BLE001
+            result["bf16_baseline"] = {"error": repr(e)}
+    del layers
+    torch.cuda.synchronize()
+    if args.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, Hv * Lyr)
+    print(json.dumps(result), flush=True)
+
+
+def run_bf16_baseline(torch, pace, args, cfg, layers):
+    B, Hv, Hk, d, dP, Lyr = cfg.B, cfg.Hv, cfg.Hk, cfg.dk, cfg.dP, args.layers
+    bcfg = pace.LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=cfg.group, bf16_io=True, dP=dP)
+    states = [torch.randn((B, Hv, d, d), device="cuda").mul_(0.05).to(torch.bfloat16) for _ in range(Lyr)]
+    stream = torch.cuda.Stream()
+    calls = []
+    for t in range(dP):
+        for l, ly in enumerate(layers):
+            q, k, v, a, b_ = ly["toks"][t]
+            calls.append(pace.prepare_bf16_decode_step(bcfg, states[l], q, k, v, a, b_, ly["o"], stream=stream))
+    with torch.cuda.stream(stream):
+        for c in calls:
+            c()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for c in calls:
+            c()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            graph.replay()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    tps = B * dP * args.steps / (ms / 1e3)
+    per_launch = B * Hv * (2 * d * d * 2 + (2 * d * 2) / (Hv // Hk) + 2 * d * 2 + 8)
+    gbs = per_launch * dP * Lyr * args.steps / (ms / 1e3) / 1e9
+    kms = kernel_durations(torch, stream, calls, periods=1).mean(axis=0)
+    kgbs = per_launch / (kms.mean() / 1e3) / 1e9
+    log(f"bf16 per-token baseline: {tps:,.0f} tok/s, {gbs:.0f} GB/s over the timed region, "
+        f"kernel mean {kms.mean() * 1e3:.2f} us = {kgbs:.0f} GB/s in-kernel")
+    del states
+    return {"value": round(tps, 1), "unit": "tokens/s", "timed_region_GBps": round(gbs, 1),
+            "bytes_per_launch": per_launch, "mean_launch_us": round(float(kms.mean()) * 1e3, 3),
+            "in_kernel_GBps": round(kgbs, 1)}
+
+
+def cpu_baseline(args, tiles_per_token):
+    """fp64 oracle (as written, untuned) on a bounded sample of the same workload: the
+    PACE-4 layer shape, a handful of (sequence, head) tiles, decode steps covering a
+    flush, from a seeded random packed state.  Reported as decode tokens/s of the full
+    stack, i.e. tile-steps/s divided by the tiles one token needs (heads x layers)."""
+    from oracle import packing as pk
+    from pace_synth import make_tokens, random_buffer_parts, random_packed_state_parts
+    d, Hv, Hk, dP = args.dim, args.heads, args.kv_heads, args.dP
+    Bs = 2
+    ocfg = pk.LayerCfg(B=Bs, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, asym=False, buf="int8", dP=dP, bf16_io=True)
+    st = pk.pack_state(ocfg, pk.state_from_parts(ocfg, random_packed_state_parts(5, Bs, Hv, d, d, 64, [4] * Hv, False)))
+    bu = pk.pack_buffer(ocfg, random_buffer_parts(6, Bs, Hv, Hk, d, d, dP, False, counts=[0] * Bs))
+    toks = make_tokens(7, Bs, 64, Hv, Hk, d, d, bf16=True)
+    tiles = [(b, h) for b in range(Bs) for h in range(0, Hv, 4)]
+    t0 = time.time()
+    steps = 0
+    while True:
+        o, st, bu, _ = pk.decode_step_layer(ocfg, st, bu, *toks.token(steps % 64), tiles=tiles)
+        steps += 1
+        if time.time() - t0 > args.cpu_seconds and steps % dP == 0:
+            break
+    el = time.time() - t0
+    tile_steps = steps * len(tiles)
+    threads = os.environ.get("OMP_NUM_THREADS", "unset")
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": round(tile_steps / el / tiles_per_token, 3), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{tile_steps} tile-steps ({len(tiles)} (seq, head) tiles x {steps} decode steps incl. "
+                      f"{steps // dP} flushes) of the PACE-4 layer shape in {el:.1f}s, single-threaded "
+                      f"Python/NumPy fp64; tokens/s = tile-steps/s / ({tiles_per_token} tiles per token); "
+                      f"host affinity {cores} cores, OMP_NUM_THREADS={threads}"}
+
+
+if __name__ == "__main__":
+    main()

@@ -226,3 +226,48 @@ def bf16_decode_step(cfg: LayerConfig, state, q, k, v, a, beta, o, stream=None):
         _ptr(beta, "beta", torch.float32, cfg.B * cfg.Hv), _ptr(o, "o", io, cfg.B * cfg.Hv * cfg.dv),
         _stream(stream))
     _check(st, "pace_bf16_decode_step")
+
+
+def prepare_decode_step(cfg: LayerConfig, state, buffer, q, k, v, a, beta, o, active=None, stream=None):
+    """Validate and marshal the arguments of pace_decode_step once; returns a callable
+    that issues the same call again with no Python-side checks (for graph capture and
+    timing loops).  The tensors must stay alive while the callable is used."""
+    import torch
+    L = layout(cfg)
+    io = _io(cfg)
+    c = cfg._c()
+    args = (ctypes.byref(c), _ptr(state, "state", torch.uint8, L["state_bytes"]),
+            _ptr(buffer, "buffer", torch.uint8, L["buffer_bytes"]),
+            _ptr(q, "q", io, cfg.B * cfg.Hk * cfg.dk), _ptr(k, "k", io, cfg.B * cfg.Hk * cfg.dk),
+            _ptr(v, "v", io, cfg.B * cfg.Hv * cfg.dv), _ptr(a, "a", torch.float32, cfg.B * cfg.Hv),
+            _ptr(beta, "beta", torch.float32, cfg.B * cfg.Hv),
+            _ptr(active, "active", torch.uint8, cfg.B, optional=True),
+            _ptr(o, "o", io, cfg.B * cfg.Hv * cfg.dv), _stream(stream))
+    fn = LIB.pace_decode_step
+
+    def call():
+        st = fn(*args)
+        if st != PACE_OK:
+            raise PaceError(st, "pace_decode_step")
+    call._keep = (c, args)
+    return call
+
+
+def prepare_bf16_decode_step(cfg: LayerConfig, state, q, k, v, a, beta, o, stream=None):
+    """Pre-marshalled pace_bf16_decode_step (see prepare_decode_step)."""
+    import torch
+    io = _io(cfg)
+    c = cfg._c()
+    args = (ctypes.byref(c), _ptr(state, "state", torch.bfloat16, cfg.B * cfg.Hv * cfg.dv * cfg.dk),
+            _ptr(q, "q", io, cfg.B * cfg.Hk * cfg.dk), _ptr(k, "k", io, cfg.B * cfg.Hk * cfg.dk),
+            _ptr(v, "v", io, cfg.B * cfg.Hv * cfg.dv), _ptr(a, "a", torch.float32, cfg.B * cfg.Hv),
+            _ptr(beta, "beta", torch.float32, cfg.B * cfg.Hv), _ptr(o, "o", io, cfg.B * cfg.Hv * cfg.dv),
+            _stream(stream))
+    fn = LIB.pace_bf16_decode_step
+
+    def call():
+        st = fn(*args)
+        if st != PACE_OK:
+            raise PaceError(st, "pace_bf16_decode_step")
+    call._keep = (c, args)
+    return call

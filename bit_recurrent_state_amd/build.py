@@ -27,6 +27,10 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: no accumulator-register moves
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # NaN / Inf inputs are undefined by the C ABI: min / max need no NaN quieting
+    "-fno-honor-nans",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

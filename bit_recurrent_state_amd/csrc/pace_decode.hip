@@ -6,18 +6,23 @@
 // formed by replaying the buffered tokens on the last-rounded state; every dP tokens the
 // buffer is folded into the state, which is rounded once.
 //
-// One workgroup of 4 waves owns one (sequence, value head) tile.  With S_0 the
-// dequantised state, k^_i / v^_i the buffered (quantised) tokens and q the query:
-//   projections  p_i = S_0^T k^_i and r = S_0^T q run on the int8 matrix cores: the
-//                state's stored codes (A operand) times the buffer's key codes and three
-//                exact int8 pieces of q (B operand), one 32-key block per MFMA, so every
-//                MFMA lies inside one scale group; scales and zero points are applied
-//                once per (column, group) afterwards.  The integer part is exact.
+// One workgroup of 2 waves owns one (sequence, value head) tile, so all B x Hv tiles of
+// a layer are resident at once (8 workgroups per CU).  With S_0 the dequantised state,
+// k^_i / v^_i the buffered (quantised) tokens and q the query:
+//   prologue     every load that does not depend on the buffer count (state codes into
+//                registers, scales / zero points, the current token) is issued before
+//                anything waits; the buffered tokens follow the count.
+//   projections  p_i = S_0^T k^_i and r = S_0^T q on the int8 matrix cores: stored codes
+//                (A) times the buffer's key codes and three exact int8 pieces of q (B),
+//                one 32-key block per MFMA so every MFMA lies inside one scale group;
+//                scale and zero point are applied once per (column, group).
 //   replay       per value column, u_i = beta_i (v^_i - a_i y_i) with
 //                y_m <- a_i y_m + (k^_i . k^_m) u_i and y_q <- a_i y_q + (k^_i . q) u_i,
-//                which is the buffer replay written on projections; o = y_q.
-//   flush        S_n = Gamma_n S_0 + sum_i (prod_{l>i} a_l) k^_i u_i^T, then each
-//                (column, g-group) is requantised and written back in place.
+//                the buffer replay written on projections; o = y_q.
+//   flush        S_n = Gamma_n S_0 + K^ diag(prod_{l>i} a_l) U on the bf16 matrix cores:
+//                key codes (exact in bf16) times a three-piece bf16 split of the fp32
+//                weights, accumulated onto Gamma_n S_0 in fp32; every (column, g-group)
+//                is then requantised in registers and written back in place.
 // The state is read once per step and written only on flush.
 #include <hip/hip_runtime.h>
 
@@ -27,10 +32,12 @@
 namespace pace {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kWaves = 2;
+constexpr int kThreads = 64 * kWaves;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 template <bool BF16>
 __device__ inline float load_io(const void* p, size_t i) {
@@ -51,109 +58,176 @@ __device__ inline float wave_max(float x) {
 
 // Sum of the 8 signed bytes of v.
 __device__ inline int sum8(long v) {
-  int lo = (int)(v & 0xffffffffl), hi = (int)((unsigned long)v >> 32);
-  int s = __builtin_amdgcn_sdot4(lo, 0x01010101, 0, false);
-  return __builtin_amdgcn_sdot4(hi, 0x01010101, s, false);
+  const int lo = (int)(v & 0xffffffffl), hi = (int)((unsigned long)v >> 32);
+  return __builtin_amdgcn_sdot4(hi, 0x01010101, __builtin_amdgcn_sdot4(lo, 0x01010101, 0, false), false);
 }
 
-// Shared memory of one workgroup.  Vector slots 0..DPMAX-1 hold buffered tokens,
-// DPMAX..DPMAX+2 the three pieces of q.
-template <int D, int NT>
-struct Smem {
-  static constexpr int NV = NT * 16;
-  static constexpr int DPMAX = NV - 3;
-  int8_t kc[NV][D];        // B-operand codes of every slot
-  float vscale[NV];        // scale of each slot
-  float vk[DPMAX][D];      // v^ during the replay, k^ during the flush
-  float P[NV][D];          // projections, then flush weights
-  float G[NV][NV];         // Gram matrix of the slots (scaled)
-  float ga[DPMAX], gb[DPMAX];
+// Shared memory of one workgroup.  TOK = largest decode period this instantiation
+// serves; vector slots 0..TOK-1 are buffered tokens, TOK..TOK+2 the pieces of q.
+// Row strides are padded (codes: +16 bytes, projections: +4 floats) so that the 16 lanes
+// of an MFMA operand or output row group hit distinct LDS banks.
+template <int D, int TOK>
+struct alignas(16) Smem {
+  static constexpr int NV = 16 * ((TOK + 3 + 15) / 16);
+  static constexpr int CH = TOK / 8;        // 8-token chunks of the flush
+  static constexpr int KCS = D + 16;        // code row stride (bytes)
+  static constexpr int PS = D + 4;          // projection row stride (floats)
+  alignas(16) int8_t kc[NV][KCS];           // B-operand codes of every slot
+  alignas(16) union {
+    int8_t c[TOK][D];                       // int8 buffer: value codes
+    uint16_t b[TOK][D];                     // mixed buffer: bf16 values
+  } v;
+  alignas(16) union {
+    float P[NV][PS];                        // projections
+    uint16_t W[CH][4][D][8];                // flush weights: 3 bf16 pieces + zeros, [col][token]
+  } pw;
+  alignas(16) uint16_t kT[CH][D][8];        // key codes as bf16, rows in (tile, row) order
+  alignas(16) float G[NV][NV];              // Gram matrix of the slots (scaled)
+  alignas(16) uint16_t scales[D * 4];       // this tile's scales, [col][group]
+  alignas(16) uint8_t zeros[D * 4];         // this tile's zero points (raw bytes)
+  float vscale[NV];                         // key scale of each token slot / q piece scale
+  float vs[TOK], ga[TOK], gb[TOK];
   float red[3][kWaves];
   float gamma_n;
 };
 
-template <int D, int NT, int BUF, int IO>
+// HB: 4 = every head 4-bit, 8 = every head 8-bit, 0 = per-head width from the map.
+// IO: 1 = bf16 q/k/v/o, 0 = fp32.
+// GT: scale-group size (32 or 64), 0 = taken from the parameters at run time.
+// AS: 0 = symmetric, 1 = asymmetric, 2 = taken from the parameters at run time.
+template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
-  using SM = Smem<D, NT>;
+  using SM = Smem<D, TOK>;
   constexpr int NV = SM::NV;
-  constexpr int DPMAX = SM::DPMAX;
+  constexpr int NT = NV / 16;           // 16-vector MFMA column tiles
+  constexpr int QS = TOK;               // first q-piece slot
+  constexpr int CH = SM::CH;
   constexpr int KB = D / 32;            // 32-key MFMA blocks per column
   constexpr int STRIPS = D / 16;        // 16-column strips per tile
-  constexpr int SPW = (STRIPS + kWaves - 1) / kWaves;
+  constexpr int SPW = STRIPS / kWaves;  // strips per wave
   constexpr bool kBf16 = IO == 1;
   __shared__ SM sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x / p.Hv, h = blockIdx.x % p.Hv;
+  const int l16 = lane & 15, qq = lane >> 4;
+  const int h = blockIdx.x, b = blockIdx.y;
   const int kh = h / p.gamma;
-  if (p.mask && !p.mask[b]) return;
-  int32_t* countp = (int32_t*)p.buffer + (size_t)b * p.Hv + h;
-  // counts outside [0, dP) cannot come from this library; clamp so that every slot
-  // index stays inside the buffer whatever the buffer holds
-  const int n0 = min(max(*countp, 0), p.dP - 1);
-  const bool flush_only = p.flush_only != 0;
-  if (flush_only && n0 == 0) return;
-  const int n = flush_only ? n0 : n0 + 1;
-  const bool do_flush = flush_only || n >= p.dP;
 
-  // ---- state record of this tile
-  const bool is8 = (p.mask8 >> h) & 1ull;
+  // ---------------------------------------------------------------- prologue
+  // Every global load below is unconditional with an in-bounds index, so the waves
+  // issue all of them before the first wait.
+  int32_t* countp = (int32_t*)p.buffer + (size_t)b * p.Hv + h;
+  const int count_raw = *countp;
+
+  const bool is8 = HB == 8 ? true : (HB == 4 ? false : ((p.mask8 >> h) & 1ull) != 0);
   const int bits = is8 ? 8 : 4;
   const uint64_t below = h ? (p.mask8 & ((1ull << h) - 1ull)) : 0ull;
   const uint64_t n8 = (uint64_t)__popcll(below);
   uint8_t* rec = p.state + (uint64_t)b * p.seq_stride + (uint64_t)h * p.rec4 + n8 * (p.rec8 - p.rec4);
-  uint16_t* scales = (uint16_t*)(rec + (is8 ? p.scales_off8 : p.scales_off4));
-  uint8_t* zeros = rec + (is8 ? p.zeros_off8 : p.zeros_off4);
-  const int NG = D / p.group;
-  const int kb_per_group = p.group / 32;
+  uint16_t* g_scales = (uint16_t*)(rec + (is8 ? p.scales_off8 : p.scales_off4));
+  uint8_t* g_zeros = rec + (is8 ? p.zeros_off8 : p.zeros_off4);
+  const int group = GT ? GT : p.group;
+  const int NG = D / group;
+  const int kpg = group / 32;           // MFMA blocks per scale group
+  const int cbytes = D * bits / 8;      // bytes per state column
+  const bool asym = AS == 2 ? (p.asym != 0) : (AS == 1);
+  const bool flush_only = p.flush_only != 0;
 
-  // ---- buffer regions
+  // The loads are issued in the order they are consumed (the memory counters complete
+  // in order): the active flag and the current token first, so that the token can be
+  // quantised while the state codes and the buffered tokens are still in flight.
+  if (flush_only && count_raw <= 0) return;   // nothing buffered: nothing to flush
+  // branch-free: without a mask the load reads an in-bounds stand-in and is ignored
+  const uint8_t mask_v = *(p.mask ? p.mask + b : (const uint8_t*)countp);
+  const bool active = !p.mask || mask_v != 0;
+  // current token (a flush-only launch is given in-bounds stand-in pointers)
+  const int te = tid < D ? tid : D - 1;
+  const float kx = load_io<kBf16>(p.k, ((size_t)b * p.Hk + kh) * D + te);
+  const float vx = load_io<kBf16>(p.v, ((size_t)b * p.Hv + h) * D + te);
+  const float qx = load_io<kBf16>(p.q, ((size_t)b * p.Hk + kh) * D + te);
+  // gates of the current token: lane l of each wave loads element min(l, Hv-1) of this
+  // sequence's row (a vector load, issued with the others); lane h holds head h
+  const float a_row = p.a[(size_t)b * p.Hv + min(lane, p.Hv - 1)];
+  const float b_row = p.beta[(size_t)b * p.Hv + min(lane, p.Hv - 1)];
+
+  // state codes of this lane: strip st = wave + kWaves * s, column st*16 + l16, keys of
+  // quarter qq (units qq*KB .. qq*KB + KB - 1)
+  constexpr int AW = HB == 4 ? KB : 2 * KB;   // code dwords per strip and lane
+  uint32_t araw[SPW][AW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int c = (wave + kWaves * s) * 16 + l16;
+    const uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
+    if (!is8) {
+      if constexpr (KB == 4) {
+        const uint4 v = *(const uint4*)colp;
+        araw[s][0] = v.x; araw[s][1] = v.y; araw[s][2] = v.z; araw[s][3] = v.w;
+      } else {
+        const uint2 v = *(const uint2*)colp;
+        araw[s][0] = v.x; araw[s][1] = v.y;
+      }
+    } else if constexpr (HB != 4) {
+#pragma unroll
+      for (int kb = 0; kb < KB; kb += 2) {
+        const uint4 v = *(const uint4*)(colp + kb * 8);
+        araw[s][2 * kb] = v.x; araw[s][2 * kb + 1] = v.y; araw[s][2 * kb + 2] = v.z; araw[s][2 * kb + 3] = v.w;
+      }
+    }
+  }
+  // scales and zero points of the whole tile (symmetric states read the scales twice
+  // instead of a zero-point region they do not have)
+  const int sc_vec = D * NG * 2 / 16;
+  const int zp_vec = asym ? D * NG * bits / 8 / 16 : 1;
+  const uint4 sc_reg = ((const uint4*)g_scales)[min(tid, sc_vec - 1)];
+  const uint4 zp_reg = ((const uint4*)(asym ? (const uint8_t*)g_zeros : (const uint8_t*)g_scales))[min(tid, zp_vec - 1)];
+
+  // counts outside [0, dP) cannot come from this library; clamp so that every slot
+  // index stays inside the buffer whatever the buffer holds
+  const int n0 = min(max(count_raw, 0), p.dP - 1);
+  const int n = flush_only ? n0 : n0 + 1;
+  const bool do_flush = flush_only || n >= p.dP;
+
+  // buffered tokens 0..n0-1: fixed-trip vector loads with clamped indices
   const size_t kslot0 = ((size_t)b * p.Hk + kh) * p.dP;
   const size_t vslot0 = ((size_t)b * p.Hv + h) * p.dP;
   float* ks_buf = (float*)(p.buffer + p.off_ks);
   float* a_buf = (float*)(p.buffer + p.off_a);
   float* beta_buf = (float*)(p.buffer + p.off_beta);
+  constexpr int RV = D / 16;                  // 16-byte vectors per int8 code row
+  constexpr int KV4 = D / 32;                 // 16-byte vectors per 4-bit key row
+  constexpr int KIT = BUF == PACE_BUF_INT8 ? ((TOK - 1) * RV + kThreads - 1) / kThreads
+                                           : ((TOK - 1) * KV4 + kThreads - 1) / kThreads;
+  constexpr int VIT = BUF == PACE_BUF_INT8 ? KIT : ((TOK - 1) * (D / 8) + kThreads - 1) / kThreads;
+  const int kvec = BUF == PACE_BUF_INT8 ? n0 * RV : n0 * KV4;
+  const int vvec = BUF == PACE_BUF_INT8 ? n0 * RV : n0 * (D / 8);
+  const uint4* kc_buf = (const uint4*)(p.buffer + p.off_kc + kslot0 * (BUF == PACE_BUF_INT8 ? D : D / 2));
+  const uint4* v_buf = (const uint4*)(p.buffer + p.off_v + vslot0 * (BUF == PACE_BUF_INT8 ? D : 2 * D));
+  uint4 kv[KIT], vv[VIT];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) kv[it] = kc_buf[min(tid + it * kThreads, max(kvec - 1, 0))];
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) vv[it] = v_buf[min(tid + it * kThreads, max(vvec - 1, 0))];
+  const int si = min(tid, max(n0 - 1, 0));
+  const float ks_l = ks_buf[kslot0 + si], a_l = a_buf[vslot0 + si], b_l = beta_buf[vslot0 + si];
+  const float vs_l = BUF == PACE_BUF_INT8 ? ((const float*)(p.buffer + p.off_vs))[vslot0 + si] : 0.f;
+  // keep the scheduler from pulling the first uses of the token (and their waits)
+  // above the remaining load issues
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- phase 0: zero the slot codes, append the current token, load the buffer
-  for (int i = tid; i < NV * D / 16; i += kThreads) ((uint4*)&sm.kc[0][0])[i] = make_uint4(0, 0, 0, 0);
-  if (tid < NV) sm.vscale[tid] = 0.f;
-  __syncthreads();
-
-  float kx = 0.f, vx = 0.f, qx = 0.f;
-  if (!flush_only && tid < D) {
-    kx = load_io<kBf16>(p.k, ((size_t)b * p.Hk + kh) * D + tid);
-    vx = load_io<kBf16>(p.v, ((size_t)b * p.Hv + h) * D + tid);
-    qx = load_io<kBf16>(p.q, ((size_t)b * p.Hk + kh) * D + tid);
-  }
+  // ---------------------------------- current token -> buffer (loads still in flight)
   {
-    float m0 = wave_max(fabsf(kx)), m1 = wave_max(fabsf(vx)), m2 = wave_max(fabsf(qx));
+    const float m0 = wave_max(tid < D ? fabsf(kx) : 0.f);
+    const float m1 = wave_max(tid < D ? fabsf(vx) : 0.f);
+    const float m2 = wave_max(tid < D ? fabsf(qx) : 0.f);
     if (lane == 0) { sm.red[0][wave] = m0; sm.red[1][wave] = m1; sm.red[2][wave] = m2; }
   }
-  // buffered tokens 0..n0-1
-  if (BUF == PACE_BUF_INT8) {
-    const int8_t* kc_buf = (const int8_t*)(p.buffer + p.off_kc) + kslot0 * D;
-    for (int i = tid; i < n0 * D / 16; i += kThreads) ((uint4*)&sm.kc[0][0])[i] = ((const uint4*)kc_buf)[i];
-    const int8_t* vc_buf = (const int8_t*)(p.buffer + p.off_v) + vslot0 * D;
-    const float* vs_buf = (const float*)(p.buffer + p.off_vs) + vslot0;
-    for (int e = tid; e < n0 * D; e += kThreads) sm.vk[e / D][e % D] = (float)vc_buf[e] * vs_buf[e / D];
-  } else {
-    const uint8_t* kc_buf = (const uint8_t*)(p.buffer + p.off_kc) + kslot0 * (D / 2);
-    for (int e = tid; e < n0 * D / 2; e += kThreads) {
-      const int i = e / (D / 2), c = e % (D / 2), m = c / 4, w = c % 4;
-      const int byte = kc_buf[e];
-      sm.kc[i][8 * m + w] = (int8_t)((byte & 15) - 8);
-      sm.kc[i][8 * m + 4 + w] = (int8_t)((byte >> 4) - 8);
-    }
-    const uint16_t* v_buf = (const uint16_t*)(p.buffer + p.off_v) + vslot0 * D;
-    for (int e = tid; e < n0 * D; e += kThreads) sm.vk[e / D][e % D] = bf16_to_f32(v_buf[e]);
-  }
-  if (tid < n0) {
-    sm.vscale[tid] = ks_buf[kslot0 + tid];
-    sm.ga[tid] = a_buf[vslot0 + tid];
-    sm.gb[tid] = beta_buf[vslot0 + tid];
-  }
+  const float a_t = __shfl(a_row, h);
+  const float b_t = __shfl(b_row, h);
   __syncthreads();
-
+  // Inactive tiles leave here, after the barrier: an exit before it would let the
+  // compiler hold every load back until the flag has arrived.  The flag is uniform
+  // over the workgroup, so the whole tile leaves together.
+  if (!active) return;
   if (!flush_only) {
     float Mk = sm.red[0][0], Mv = sm.red[1][0], Mq = sm.red[2][0];
 #pragma unroll
@@ -161,46 +235,46 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       Mk = fmaxf(Mk, sm.red[0][w]); Mv = fmaxf(Mv, sm.red[1][w]); Mq = fmaxf(Mq, sm.red[2][w]);
     }
     const float kq_max = BUF == PACE_BUF_INT8 ? 127.f : 7.f;
-    const float ks = Mk / kq_max;      // IEEE division (fp32 buffer scale)
+    const float ks = Mk / kq_max;       // IEEE division: the fp32 buffer scale
     if (tid < D) {
       const float kcf = ks > 0.f ? fminf(fmaxf(rintf(kx / ks), -kq_max), kq_max) : 0.f;
       sm.kc[n0][tid] = (int8_t)kcf;
-      float vhat;
       int8_t vcode = 0;
       float vs = 0.f;
       if (BUF == PACE_BUF_INT8) {
         vs = Mv / 127.f;
-        const float vcf = vs > 0.f ? fminf(fmaxf(rintf(vx / vs), -127.f), 127.f) : 0.f;
-        vcode = (int8_t)vcf;
-        vhat = vcf * vs;
+        vcode = (int8_t)(vs > 0.f ? fminf(fmaxf(rintf(vx / vs), -127.f), 127.f) : 0.f);
+        sm.v.c[n0][tid] = vcode;
       } else {
-        vhat = bf16_to_f32(f32_to_bf16_rne(vx));
+        sm.v.b[n0][tid] = f32_to_bf16_rne(vx);
       }
-      sm.vk[n0][tid] = vhat;
-      // q as three exact int8 pieces with power-of-two scales s1, s1/128, s1/16384
+      // q as three exact int8 pieces with power-of-two scales s1, s1/128, s1/16384,
+      // s1 = 2^(e-6) for max|q| = m 2^e (0.5 <= m < 1), so |q / s1| < 64
+      float q1 = 0.f, q2 = 0.f, q3 = 0.f;
+      int e1 = 0;
       if (Mq > 0.f) {
-        int e1;
-        frexpf(Mq / 127.f, &e1);
-        const float q1 = rintf(ldexpf(qx, -e1));
+        frexpf(Mq, &e1);
+        e1 -= 6;
+        q1 = rintf(ldexpf(qx, -e1));
         const float r1 = qx - ldexpf(q1, e1);
-        const float q2 = rintf(ldexpf(r1, 7 - e1));
+        q2 = rintf(ldexpf(r1, 7 - e1));
         const float r2 = r1 - ldexpf(q2, e1 - 7);
-        const float q3 = rintf(ldexpf(r2, 14 - e1));
-        sm.kc[DPMAX + 0][tid] = (int8_t)q1;
-        sm.kc[DPMAX + 1][tid] = (int8_t)q2;
-        sm.kc[DPMAX + 2][tid] = (int8_t)q3;
-        if (tid == 0) {
-          sm.vscale[DPMAX + 0] = ldexpf(1.f, e1);
-          sm.vscale[DPMAX + 1] = ldexpf(1.f, e1 - 7);
-          sm.vscale[DPMAX + 2] = ldexpf(1.f, e1 - 14);
-        }
+        q3 = rintf(ldexpf(r2, 14 - e1));
       }
+      sm.kc[QS + 0][tid] = (int8_t)q1;
+      sm.kc[QS + 1][tid] = (int8_t)q2;
+      sm.kc[QS + 2][tid] = (int8_t)q3;
       if (tid == 0) {
+        const float s1 = Mq > 0.f ? ldexpf(1.f, e1) : 0.f;
+        sm.vscale[QS + 0] = s1;
+        sm.vscale[QS + 1] = s1 * 0.0078125f;
+        sm.vscale[QS + 2] = s1 * 0.00006103515625f;
         sm.vscale[n0] = ks;
-        sm.ga[n0] = p.a[(size_t)b * p.Hv + h];
-        sm.gb[n0] = p.beta[(size_t)b * p.Hv + h];
+        sm.vs[n0] = vs;
+        sm.ga[n0] = a_t;
+        sm.gb[n0] = b_t;
       }
-      // append to the buffer unless this step flushes it
+      // append to the buffer unless this step empties it
       if (!do_flush) {
         const bool key_writer = (h % p.gamma) == 0;
         if (BUF == PACE_BUF_INT8) {
@@ -212,12 +286,67 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         }
         if (tid == 0) {
           if (key_writer) ks_buf[kslot0 + n0] = ks;
-          a_buf[vslot0 + n0] = p.a[(size_t)b * p.Hv + h];
-          beta_buf[vslot0 + n0] = p.beta[(size_t)b * p.Hv + h];
+          a_buf[vslot0 + n0] = a_t;
+          beta_buf[vslot0 + n0] = b_t;
         }
       }
     }
   }
+
+  // ---------------------------------------------------------------- LDS fills
+  if (BUF == PACE_BUF_INT8) {
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int i = tid + it * kThreads;
+      if (i < kvec) {
+        *(uint4*)&sm.kc[i / RV][16 * (i % RV)] = kv[it];
+        ((uint4*)&sm.v.c[0][0])[i] = vv[it];
+      }
+    }
+    if (tid < n0) sm.vs[tid] = vs_l;
+  } else {
+    // 4-bit keys: 16 bytes = four 8-key units; byte w of unit m holds keys 8m+w (low
+    // nibble) and 8m+4+w (high nibble), each stored as c + 8.
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int i = tid + it * kThreads;
+      if (i < kvec) {
+        const uint32_t w4[4] = {kv[it].x, kv[it].y, kv[it].z, kv[it].w};
+        uint32_t out[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          // per byte, (x | 0x80) - 8 never borrows; ^ 0x80 leaves the code c = x - 8
+          const uint32_t lo = w4[m] & 0x0F0F0F0Fu, hi = (w4[m] >> 4) & 0x0F0F0F0Fu;
+          out[2 * m] = ((lo | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
+          out[2 * m + 1] = ((hi | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
+        }
+        int8_t* dst = &sm.kc[i / KV4][32 * (i % KV4)];
+        *(uint4*)dst = make_uint4(out[0], out[1], out[2], out[3]);
+        *(uint4*)(dst + 16) = make_uint4(out[4], out[5], out[6], out[7]);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int i = tid + it * kThreads;
+      if (i < vvec) ((uint4*)&sm.v.b[0][0])[i] = vv[it];
+    }
+  }
+  if (tid < n0) {
+    sm.vscale[tid] = ks_l;
+    sm.ga[tid] = a_l;
+    sm.gb[tid] = b_l;
+  }
+  // unused token slots (n .. TOK-1) and, without a query, the q slots hold zeros
+#pragma unroll
+  for (int it = 0; it < (NV * RV + kThreads - 1) / kThreads; ++it) {
+    const int i = tid + it * kThreads;
+    const int row = i / RV;
+    if (i < NV * RV && row >= n && (row < QS || flush_only || row >= QS + 3))
+      *(uint4*)&sm.kc[row][16 * (i % RV)] = make_uint4(0, 0, 0, 0);
+  }
+  if (tid >= n && tid < NV && (tid < QS || flush_only || tid >= QS + 3)) sm.vscale[tid] = 0.f;
+  if (tid < sc_vec) ((uint4*)sm.scales)[tid] = sc_reg;
+  if (asym && tid < zp_vec) ((uint4*)sm.zeros)[tid] = zp_reg;
   __syncthreads();
   if (BUF == PACE_BUF_K4_VBF16 && !flush_only && !do_flush && (h % p.gamma) == 0 && tid < D / 2) {
     const int m = tid / 4, w = tid % 4;
@@ -225,8 +354,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     ((uint8_t*)(p.buffer + p.off_kc))[(kslot0 + n0) * (D / 2) + tid] = (uint8_t)(lo | (hi << 4));
   }
 
-  // ---- phase 1: B operands, group sums, Gram matrix, projections
-  const int l16 = lane & 15, qq = lane >> 4;
+  // --------------------------------------------- B operands, group sums, Gram
   long bop[NT][KB];
   int ksum[NT][4];
 #pragma unroll
@@ -237,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     for (int kb = 0; kb < KB; ++kb) {
       bop[nt][kb] = *(const long*)&sm.kc[nt * 16 + l16][32 * kb + 8 * qq];
       const int s = sum8(bop[nt][kb]);
-      const int g = kb / kb_per_group;
+      const int g = kb / kpg;
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) ksum[nt][gg] += (gg == g) ? s : 0;
     }
@@ -247,9 +375,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       ksum[nt][g] += __shfl_xor(ksum[nt][g], 32);
     }
   }
-  if (wave == 0) {
+  if (wave == kWaves - 1) {
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
+    for (int mt = 0; mt < NT; ++mt) {
+      if (mt * 16 >= n && mt * 16 < QS) continue;     // row tiles of empty token slots
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         v4i acc = {0, 0, 0, 0};
@@ -262,36 +391,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           sm.G[row][col] = (float)acc[i] * sm.vscale[row] * sm.vscale[col];
         }
       }
+    }
   }
 
-  const int cbytes = D * bits / 8;     // bytes per state column
-  uint32_t araw[SPW][2 * KB];          // raw codes of this lane, kept for the flush
+  // ------------------------------------------------------------ projections
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
-    const int st = wave + s * kWaves;
-    if (st >= STRIPS) break;
-    const int col0 = st * 16;
-    const uint8_t* colp = rec + (size_t)(col0 + l16) * cbytes + qq * KB * bits;
-    if (!is8) {
-#pragma unroll
-      for (int kb = 0; kb < KB; kb += 4 > KB ? KB : 4) {
-        if constexpr (KB >= 4) {
-          const uint4 v = *(const uint4*)(colp + kb * 4);
-          araw[s][kb] = v.x; araw[s][kb + 1] = v.y; araw[s][kb + 2] = v.z; araw[s][kb + 3] = v.w;
-        } else {
-          const uint2 v = *(const uint2*)(colp + kb * 4);
-          araw[s][kb] = v.x; araw[s][kb + 1] = v.y;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < KB; kb += 2) {
-        const uint4 v = *(const uint4*)(colp + kb * 8);
-        araw[s][2 * kb] = v.x; araw[s][2 * kb + 1] = v.y; araw[s][2 * kb + 2] = v.z; araw[s][2 * kb + 3] = v.w;
-      }
-    }
-    // scales / zero points of the 4 output columns col0 + 4qq + i of this lane
-    const int ocol = col0 + 4 * qq;
+    const int col0 = (wave + kWaves * s) * 16;
+    const int ocol = col0 + 4 * qq;     // output columns ocol + i of this lane
     float proj[NT][4];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -305,29 +412,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       long a;
       if (!is8) {
         const uint32_t d = araw[s][kb];
-        const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
-        a = (long)(((unsigned long)hi << 32) | lo);
-      } else {
-        const uint32_t lo = araw[s][2 * kb] ^ 0x80808080u, hi = araw[s][2 * kb + 1] ^ 0x80808080u;
-        a = (long)(((unsigned long)hi << 32) | lo);
+        a = (long)(((unsigned long)((d >> 4) & 0x0F0F0F0Fu) << 32) | (d & 0x0F0F0F0Fu));
+      } else if constexpr (HB != 4) {
+        a = (long)(((unsigned long)(araw[s][2 * kb + 1] ^ 0x80808080u) << 32) | (araw[s][2 * kb] ^ 0x80808080u));
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bop[nt][kb], acc[nt], 0, 0, 0);
-      if ((kb + 1) % kb_per_group != 0) continue;
-      // end of scale group g: apply scale and zero point once per (column, group)
-      const int g = kb / kb_per_group;
+      if ((kb + 1) % kpg != 0) continue;
+      // end of scale group g: scale and zero point once per (column, group)
+      const int g = kb / kpg;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = ocol + i;
-        const float sc = bf16_to_f32(scales[c * NG + g]);
+        const float sc = bf16_to_f32(sm.scales[c * NG + g]);
         int z;
-        if (p.asym) {
+        if (asym) {
           const int e = c * NG + g;
-          z = is8 ? (int)zeros[e] : (int)((zeros[e >> 1] >> (4 * (e & 1))) & 15);
+          z = is8 ? (int)sm.zeros[e] : (int)((sm.zeros[e >> 1] >> (4 * (e & 1))) & 15);
         } else {
           z = 1 << (bits - 1);
         }
-        if (is8) z -= 128;                   // A operand held codes - 128
+        if (is8) z -= 128;                // the A operand held codes - 128
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           int ksg = 0;
@@ -343,194 +448,236 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     for (int nt = 0; nt < NT; ++nt) {
       const int vi = nt * 16 + l16;
       const float vsc = sm.vscale[vi];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.P[vi][ocol + i] = proj[nt][i] * vsc;
+      *(float4*)&sm.pw.P[vi][ocol] = make_float4(proj[nt][0] * vsc, proj[nt][1] * vsc, proj[nt][2] * vsc, proj[nt][3] * vsc);
     }
   }
   __syncthreads();
 
-  // ---- phase 2: replay on projections, one value column per thread
+  // -------------------------------------------- replay, one value column / thread
+  float u[TOK];
   if (tid < D) {
     const int j = tid;
-    float y[DPMAX], u[DPMAX];
+    float y[TOK];
 #pragma unroll
-    for (int m = 0; m < DPMAX; ++m) { y[m] = (m < n) ? sm.P[m][j] : 0.f; u[m] = 0.f; }
-    float yq = sm.P[DPMAX][j] + sm.P[DPMAX + 1][j] + sm.P[DPMAX + 2][j];
+    for (int m = 0; m < TOK; ++m) { y[m] = (m < n) ? sm.pw.P[m][j] : 0.f; u[m] = 0.f; }
+    float yq = sm.pw.P[QS][j] + sm.pw.P[QS + 1][j] + sm.pw.P[QS + 2][j];
 #pragma unroll
-    for (int i = 0; i < DPMAX; ++i) {
+    for (int i = 0; i < TOK; ++i) {
       if (i < n) {
         const float ai = sm.ga[i];
-        const float ui = sm.gb[i] * (sm.vk[i][j] - ai * y[i]);
+        const float vh = BUF == PACE_BUF_INT8 ? (float)sm.v.c[i][j] * sm.vs[i] : bf16_to_f32(sm.v.b[i][j]);
+        const float ui = sm.gb[i] * (vh - ai * y[i]);
         u[i] = ui;
 #pragma unroll
-        for (int m = i + 1; m < DPMAX; ++m)
+        for (int m = i + 1; m < TOK; ++m)
           if (m < n) y[m] = ai * y[m] + sm.G[i][m] * ui;
-        const float gq = sm.G[i][DPMAX] + sm.G[i][DPMAX + 1] + sm.G[i][DPMAX + 2];
+        const float gq = sm.G[i][QS] + sm.G[i][QS + 1] + sm.G[i][QS + 2];
         yq = ai * yq + gq * ui;
       }
     }
     if (!flush_only) store_io<kBf16>(p.o, ((size_t)b * p.Hv + h) * D + j, yq);
-    if (do_flush) {
-      float w = 1.f;
-#pragma unroll
-      for (int i = DPMAX - 1; i >= 0; --i) {
-        if (i < n) {
-          sm.P[i][j] = w * u[i];
-          w *= sm.ga[i];
-        }
-      }
-      if (j == 0) sm.gamma_n = w;
-    }
   }
   if (!do_flush) {
     if (tid == 0) *countp = n;
     return;
   }
-  __syncthreads();
-  for (int e = tid; e < n * D; e += kThreads) sm.vk[e / D][e % D] = (float)sm.kc[e / D][e % D] * sm.vscale[e / D];
+  __syncthreads();        // every projection is read: the weights may overwrite them
+
+  // ------------------------------------------------------------ flush: weights
+  // W_i[j] = k-scale_i * prod_{l>i} a_l * u_i[j], split into three bf16 pieces; key
+  // codes transposed to [key][token] bf16 for the A operand.
+  if (tid < D) {
+    const int j = tid;
+    float w = 1.f;
+    uint32_t pk[3][TOK / 2];              // pieces, two bf16 per dword, token order
+#pragma unroll
+    for (int i = 0; i < TOK / 2; ++i) pk[0][i] = pk[1][i] = pk[2][i] = 0u;
+#pragma unroll
+    for (int i = TOK - 1; i >= 0; --i) {
+      float wi = 0.f;
+      if (i < n) {
+        wi = w * sm.vscale[i] * u[i];
+        w *= sm.ga[i];
+      }
+      const uint16_t h0 = f32_to_bf16_rne(wi);
+      const float r0 = wi - bf16_to_f32(h0);
+      const uint16_t h1 = f32_to_bf16_rne(r0);
+      const uint16_t h2 = f32_to_bf16_rne(r0 - bf16_to_f32(h1));
+      const int sh = 16 * (i & 1);
+      pk[0][i / 2] |= (uint32_t)h0 << sh;
+      pk[1][i / 2] |= (uint32_t)h1 << sh;
+      pk[2][i / 2] |= (uint32_t)h2 << sh;
+    }
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) {
+#pragma unroll
+      for (int pc = 0; pc < 3; ++pc)
+        *(uint4*)&sm.pw.W[ch][pc][j][0] = make_uint4(pk[pc][4 * ch], pk[pc][4 * ch + 1], pk[pc][4 * ch + 2], pk[pc][4 * ch + 3]);
+      *(uint4*)&sm.pw.W[ch][3][j][0] = make_uint4(0, 0, 0, 0);   // lanes of quarter 3 add nothing
+    }
+    if (j == 0) sm.gamma_n = w;
+    // key j sits in accumulator tile t = 2 (j / 32) + (j % 8) / 4, row m = 4 ((j % 32) / 8) + j % 4
+    const int t = 2 * (j / 32) + (j % 8) / 4, m = 4 * ((j % 32) / 8) + (j % 4);
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) {
+      uint32_t kw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i0 = 8 * ch + 2 * e, i1 = i0 + 1;
+        const int8_t c0 = i0 < n ? sm.kc[i0][j] : (int8_t)0;
+        const int8_t c1 = i1 < n ? sm.kc[i1][j] : (int8_t)0;
+        kw[e] = (f32_bits((float)c0) >> 16) | (f32_bits((float)c1) & 0xFFFF0000u);   // exact in bf16
+      }
+      *(uint4*)&sm.kT[ch][t * 16 + m][0] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+    }
+  }
   __syncthreads();
 
-  // ---- phase 3: fold the buffer in and requantise each (column, group) once
-  const float gamma_n = sm.gamma_n;
-  const int levels = (1 << bits) - 1;
-  const int zsym = 1 << (bits - 1);
-  const float qmax = (float)(zsym - 1);
+  // ----------------------------------------- flush: fold on MFMA, requantise
+  const float gn = sm.gamma_n;
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
-    const int st = wave + s * kWaves;
-    if (st >= STRIPS) break;
-    const int c = st * 16 + l16;
-    float x[KB][8];
+    const int c = (wave + kWaves * s) * 16 + l16;    // this lane's column
+    // accumulator tile t = 2 kb + half holds keys 32 kb + 8 qq + 4 half + i
+    v4f acc[2 * KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int g = kb / kb_per_group;
-      const float sc = bf16_to_f32(scales[c * NG + g]);
+      const int g = kb / kpg;
+      const float sc = bf16_to_f32(sm.scales[c * NG + g]);
       int z;
-      if (p.asym) {
+      if (asym) {
         const int e = c * NG + g;
-        z = is8 ? (int)zeros[e] : (int)((zeros[e >> 1] >> (4 * (e & 1))) & 15);
+        z = is8 ? (int)sm.zeros[e] : (int)((sm.zeros[e >> 1] >> (4 * (e & 1))) & 15);
       } else {
-        z = zsym;
+        z = 1 << (bits - 1);
       }
-      const float gs = gamma_n * sc;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int code;
-        if (!is8) code = (araw[s][kb] >> (8 * (e & 3) + 4 * (e >> 2))) & 15;
-        else code = (araw[s][2 * kb + (e >> 2)] >> (8 * (e & 3))) & 255;
-        x[kb][e] = gs * (float)(code - z);
+      const float gs = gn * sc, gz = -gs * (float)z;
+      uint32_t b0, b1;            // 4 stored codes each (bytes): keys +0..3, +4..7
+      if (!is8) {
+        b0 = araw[s][kb] & 0x0F0F0F0Fu;
+        b1 = (araw[s][kb] >> 4) & 0x0F0F0F0Fu;
+      } else if constexpr (HB != 4) {
+        b0 = araw[s][2 * kb];
+        b1 = araw[s][2 * kb + 1];
       }
+      // byte i of b0 / b1 -> float via the per-byte conversions
+      acc[2 * kb][0] = fmaf((float)(b0 & 255u), gs, gz);
+      acc[2 * kb][1] = fmaf((float)((b0 >> 8) & 255u), gs, gz);
+      acc[2 * kb][2] = fmaf((float)((b0 >> 16) & 255u), gs, gz);
+      acc[2 * kb][3] = fmaf((float)(b0 >> 24), gs, gz);
+      acc[2 * kb + 1][0] = fmaf((float)(b1 & 255u), gs, gz);
+      acc[2 * kb + 1][1] = fmaf((float)((b1 >> 8) & 255u), gs, gz);
+      acc[2 * kb + 1][2] = fmaf((float)((b1 >> 16) & 255u), gs, gz);
+      acc[2 * kb + 1][3] = fmaf((float)(b1 >> 24), gs, gz);
     }
-    for (int i = 0; i < n; ++i) {
-      const float wi = sm.P[i][c];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const float4 k0 = *(const float4*)&sm.vk[i][32 * kb + 8 * qq];
-        const float4 k1 = *(const float4*)&sm.vk[i][32 * kb + 8 * qq + 4];
-        x[kb][0] += k0.x * wi; x[kb][1] += k0.y * wi; x[kb][2] += k0.z * wi; x[kb][3] += k0.w * wi;
-        x[kb][4] += k1.x * wi; x[kb][5] += k1.y * wi; x[kb][6] += k1.z * wi; x[kb][7] += k1.w * wi;
-      }
+    for (int ch = 0; ch < CH; ++ch) {
+      if (ch * 8 >= n) break;
+      // K index 8 qq + token: quarters 0..2 carry the three weight pieces, quarter 3 a
+      // zero piece, so the key codes can be loaded by every lane unconditionally
+      const v8bf bw = *(const v8bf*)&sm.pw.W[ch][qq][c][0];
+      v8bf ak[2 * KB];
+#pragma unroll
+      for (int t = 0; t < 2 * KB; ++t) ak[t] = *(const v8bf*)&sm.kT[ch][t * 16 + l16][0];
+#pragma unroll
+      for (int t = 0; t < 2 * KB; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[t], bw, acc[t], 0, 0, 0);
     }
-    uint32_t out[2 * KB];
+    // requantise each (column, group) and write back in place
+    uint32_t outw[AW];
 #pragma unroll
-    for (int i = 0; i < 2 * KB; ++i) out[i] = 0;
+    for (int i = 0; i < AW; ++i) outw[i] = 0;
     int zprev = 0;
-    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (g >= NG) break;
       float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        if (kb / kb_per_group != g) continue;
+        if (kb / kpg != g) continue;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { mx = fmaxf(mx, x[kb][e]); mn = fminf(mn, x[kb][e]); }
+        for (int i = 0; i < 4; ++i) {
+          mx = fmaxf(mx, fmaxf(acc[2 * kb][i], acc[2 * kb + 1][i]));
+          mn = fminf(mn, fminf(acc[2 * kb][i], acc[2 * kb + 1][i]));
+        }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16)); mx = fmaxf(mx, __shfl_xor(mx, 32));
       mn = fminf(mn, __shfl_xor(mn, 16)); mn = fminf(mn, __shfl_xor(mn, 32));
-      float sn;
-      int z;
-      if (!p.asym) {
-        const float M = fmaxf(fabsf(mx), fabsf(mn));
-        sn = bf16_ceil_from_f64((double)M / (double)qmax);
-        z = zsym;
-      } else {
-        const float lo = fminf(mn, 0.f), hi = fmaxf(mx, 0.f);
-        sn = bf16_ceil_from_f64(((double)hi - (double)lo) / (double)levels);
-        z = 0;
-        if (sn > 0.f) z = (int)fminf(fmaxf(rne_quotient(-lo, sn, 1.f / sn), 0.f), (float)levels);
-      }
-      const float r = sn > 0.f ? 1.f / sn : 0.f;
+      const GroupQuant gq = group_quant(mn, mx, asym, bits);
+      const CodeRange cr = code_range(gq.z, asym, bits);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        if (kb / kb_per_group != g) continue;
+        if (kb / kpg != g) continue;
+        uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          int code;
-          if (sn == 0.f) {
-            code = p.asym ? 0 : zsym;
-          } else if (!p.asym) {
-            code = (int)fminf(fmaxf(rne_quotient(x[kb][e], sn, r), -qmax), qmax) + zsym;
-          } else {
-            code = (int)fminf(fmaxf(rne_quotient(x[kb][e], sn, r) + (float)z, 0.f), (float)levels);
-          }
-          if (!is8) out[kb] |= (uint32_t)code << (8 * (e & 3) + 4 * (e >> 2));
-          else out[2 * kb + (e >> 2)] |= (uint32_t)code << (8 * (e & 3));
+        for (int i = 0; i < 4; ++i) {
+          lo |= (uint32_t)code_of(acc[2 * kb][i], gq.r, cr.magic, cr.lo, cr.hi) << (8 * i);
+          hi |= (uint32_t)code_of(acc[2 * kb + 1][i], gq.r, cr.magic, cr.lo, cr.hi) << (8 * i);
+        }
+        if (!is8) {
+          outw[kb] = lo | (hi << 4);
+        } else if constexpr (HB != 4) {
+          outw[2 * kb] = lo;
+          outw[2 * kb + 1] = hi;
         }
       }
       if (qq == 0) {
-        scales[c * NG + g] = (uint16_t)(f32_bits(sn) >> 16);
-        if (p.asym) {
+        g_scales[c * NG + g] = (uint16_t)(f32_bits(gq.s) >> 16);
+        if (asym) {
           const int e = c * NG + g;
-          if (is8) zeros[e] = (uint8_t)z;
-          else if (e & 1) zeros[e >> 1] = (uint8_t)(zprev | (z << 4));
+          if (is8) g_zeros[e] = (uint8_t)gq.z;
+          else if (e & 1) g_zeros[e >> 1] = (uint8_t)(zprev | (gq.z << 4));
         }
       }
-      zprev = z;
+      zprev = gq.z;
     }
     uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
     if (!is8) {
-      if constexpr (KB >= 4) {
-#pragma unroll
-        for (int kb = 0; kb < KB; kb += 4) *(uint4*)(colp + kb * 4) = make_uint4(out[kb], out[kb + 1], out[kb + 2], out[kb + 3]);
-      } else {
-        *(uint2*)colp = make_uint2(out[0], out[1]);
-      }
-    } else {
+      if constexpr (KB == 4) *(uint4*)colp = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+      else *(uint2*)colp = make_uint2(outw[0], outw[1]);
+    } else if constexpr (HB != 4) {
 #pragma unroll
       for (int kb = 0; kb < KB; kb += 2)
-        *(uint4*)(colp + kb * 8) = make_uint4(out[2 * kb], out[2 * kb + 1], out[2 * kb + 2], out[2 * kb + 3]);
+        *(uint4*)(colp + kb * 8) = make_uint4(outw[2 * kb], outw[2 * kb + 1], outw[2 * kb + 2], outw[2 * kb + 3]);
     }
   }
   if (tid == 0) *countp = 0;
 }
 
-template <int D, int NT, int BUF, int IO>
+template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const unsigned grid = (unsigned)p.B * (unsigned)p.Hv;
-  hipLaunchKernelGGL((decode_kernel<D, NT, BUF, IO>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<D, TOK, BUF, HB, IO, GT, AS>), dim3((unsigned)p.Hv, (unsigned)p.B), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int BUF, int IO>
-hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
-  // slots: dP tokens + 3 pieces of q, 16 per MFMA column tile
-  if (p.dP <= 13) return launch_t<D, 1, BUF, IO>(p, stream);
-  if (p.dP <= 29) return launch_t<D, 2, BUF, IO>(p, stream);
-  return launch_t<D, 3, BUF, IO>(p, stream);
+// Specialised instantiations for the layouts the method names (d = 128, dP <= 8, bf16
+// I/O; 64-key symmetric and 32-key asymmetric groups, and their mirror images), with
+// group size and symmetry known at compile time.
+template <int BUF, int HB>
+hipError_t launch_fast(const DecodeParams& p, hipStream_t stream) {
+  if (p.group == 64) return p.asym ? launch_t<128, 8, BUF, HB, 1, 64, 1>(p, stream) : launch_t<128, 8, BUF, HB, 1, 64, 0>(p, stream);
+  return p.asym ? launch_t<128, 8, BUF, HB, 1, 32, 1>(p, stream) : launch_t<128, 8, BUF, HB, 1, 32, 0>(p, stream);
 }
 
-template <int D>
-hipError_t launch_d(const DecodeParams& p, int io_bf16, int buf_kind, hipStream_t stream) {
-  if (buf_kind == PACE_BUF_INT8)
-    return io_bf16 ? launch_nt<D, PACE_BUF_INT8, 1>(p, stream) : launch_nt<D, PACE_BUF_INT8, 0>(p, stream);
-  return io_bf16 ? launch_nt<D, PACE_BUF_K4_VBF16, 1>(p, stream) : launch_nt<D, PACE_BUF_K4_VBF16, 0>(p, stream);
+template <int D, int BUF, int IO>
+hipError_t launch_generic(const DecodeParams& p, hipStream_t stream) {
+  if (p.dP <= 8) return launch_t<D, 8, BUF, 0, IO, 0, 2>(p, stream);
+  return launch_t<D, 32, BUF, 0, IO, 0, 2>(p, stream);
+}
+
+template <int BUF>
+hipError_t launch_buf(const DecodeParams& p, int dk, hipStream_t stream) {
+  if (dk == 128 && p.dP <= 8 && p.io_bf16)
+    return p.mask8 == 0 ? launch_fast<BUF, 4>(p, stream) : launch_fast<BUF, 0>(p, stream);
+  if (dk == 128) return p.io_bf16 ? launch_generic<128, BUF, 1>(p, stream) : launch_generic<128, BUF, 0>(p, stream);
+  return p.io_bf16 ? launch_generic<64, BUF, 1>(p, stream) : launch_generic<64, BUF, 0>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int dk, int dv, int io_bf16, int buf_kind,
-                         hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int dk, int dv, int buf_kind, hipStream_t stream) {
   (void)dv;  // dk == dv is validated by the caller
-  if (dk == 128) return launch_d<128>(p, io_bf16, buf_kind, stream);
-  return launch_d<64>(p, io_bf16, buf_kind, stream);
+  if (buf_kind == PACE_BUF_INT8) return launch_buf<PACE_BUF_INT8>(p, dk, stream);
+  return launch_buf<PACE_BUF_K4_VBF16>(p, dk, stream);
 }
 
 }  // namespace pace

@@ -157,8 +157,8 @@ pace_status pace_decode_step(const pace_layer_cfg* cfg, void* state, void* buffe
   p.B = cfg->B; p.Hv = cfg->Hv; p.Hk = cfg->Hk; p.gamma = cfg->Hv / cfg->Hk;
   p.dP = cfg->dP; p.group = cfg->group; p.asym = cfg->state_kind == PACE_STATE_ASYM;
   p.flush_only = 0;
-  const hipError_t e = launch_decode(p, cfg->dk, cfg->dv, cfg->io_dtype == PACE_IO_BF16,
-                                     cfg->buf_kind, (hipStream_t)stream);
+  p.io_bf16 = cfg->io_dtype == PACE_IO_BF16;
+  const hipError_t e = launch_decode(p, cfg->dk, cfg->dv, cfg->buf_kind, (hipStream_t)stream);
   return e == hipSuccess ? PACE_OK : PACE_EHIP;
 }
 
@@ -184,8 +184,13 @@ pace_status pace_flush_requant(const pace_layer_cfg* cfg, void* state, void* buf
   p.B = cfg->B; p.Hv = cfg->Hv; p.Hk = cfg->Hk; p.gamma = cfg->Hv / cfg->Hk;
   p.dP = cfg->dP; p.group = cfg->group; p.asym = cfg->state_kind == PACE_STATE_ASYM;
   p.flush_only = 1;
-  const hipError_t e = launch_decode(p, cfg->dk, cfg->dv, cfg->io_dtype == PACE_IO_BF16,
-                                     cfg->buf_kind, (hipStream_t)stream);
+  p.io_bf16 = cfg->io_dtype == PACE_IO_BF16;
+  // no token: the kernel's unconditional token loads read the state instead (every index
+  // they form is below B * Hk * dk * 4 bytes, which the state always exceeds) and never
+  // use the values
+  p.q = p.k = p.v = state;
+  p.a = p.beta = (const float*)state;
+  const hipError_t e = launch_decode(p, cfg->dk, cfg->dv, cfg->buf_kind, (hipStream_t)stream);
   return e == hipSuccess ? PACE_OK : PACE_EHIP;
 }
 

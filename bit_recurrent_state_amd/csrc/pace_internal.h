@@ -77,6 +77,7 @@ struct DecodeParams {
   uint64_t off_kc, off_ks, off_v, off_vs, off_a, off_beta;  // buffer regions
   int32_t B, Hv, Hk, gamma, dP, group, asym;
   int32_t flush_only;   // 1: pace_flush_requant (no new token)
+  int32_t io_bf16;      // q, k, v, o are bf16 (else fp32)
 };
 
 struct PrefillParams {
@@ -107,8 +108,7 @@ struct Bf16Params {
 };
 
 // Launchers (defined next to their kernels).  They only enqueue work.
-hipError_t launch_decode(const DecodeParams& p, int dk, int dv, int io_bf16, int buf_kind,
-                         hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int dk, int dv, int buf_kind, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dk, int dv, int io_bf16,
                           hipStream_t stream);
 size_t prefill_workspace_bytes(int B, int Hv, int dk, int dv, int T, int chunk);

@@ -56,6 +56,20 @@ __host__ __device__ inline float bf16_ceil_from_f64(double d) {
   return bits_f32(u);
 }
 
+// Smallest bf16 value >= m / k for fp32 m >= 0 and a small positive integer k, without
+// leaving fp32: q = fl(m / k) is correctly rounded; if q * k < m (decided exactly by one
+// fused multiply-add, whose product q * k needs at most 24 + 8 bits) the quotient was
+// rounded down and q is moved one fp32 ulp up; the result is then rounded up to bf16.
+// Exact because bf16 values are fp32 values.
+__host__ __device__ inline float bf16_ceil_div(float m, float k) {
+  if (!(m > 0.0f)) return 0.0f;
+  float q = m / k;
+  if (fmaf(q, k, -m) < 0.0f) q = bits_f32(f32_bits(q) + 1u);
+  uint32_t u = f32_bits(q);
+  if (u & 0xFFFFu) u = (u + 0x10000u) & 0xFFFF0000u;
+  return bits_f32(u);
+}
+
 // round-half-to-even(x / s) for fp32 x and a bf16-valued scale s > 0, exactly.
 // r = 1/s (any fp32 approximation).  A first guess n = rne(x * r) is within one of the
 // answer; the residual e = x - n*s is exact in fp32 (s has 8 significant bits and
@@ -77,6 +91,59 @@ __host__ __device__ inline float rne_quotient(float x, float s, float r) {
     if (fmodf(n, 2.0f) != 0.0f) n = alt;
   }
   return n;
+}
+
+// Group parameters of the quantiser from the group's min and max (fp32 pre-rounding
+// values).  Symmetric: s = bf16_ceil(max|x| / (2^(b-1)-1)), z = 2^(b-1).  Asymmetric:
+// lo = min(0, min), hi = max(0, max), s = bf16_ceil((hi - lo) / (2^b - 1)),
+// z = clip(rne(-lo / s), 0, 2^b - 1) decided exactly.  s = 0 gives z = 0 (asym).
+struct GroupQuant {
+  float s, r;   // scale and its reciprocal (0 when s = 0)
+  int z;        // zero point / stored offset
+};
+
+__host__ __device__ inline GroupQuant group_quant(float mn, float mx, bool asym, int bits) {
+  GroupQuant q;
+  const int levels = (1 << bits) - 1, zsym = 1 << (bits - 1);
+  if (!asym) {
+    const float M = fmaxf(fabsf(mx), fabsf(mn));
+    q.s = bf16_ceil_div(M, (float)(zsym - 1));
+    q.z = zsym;
+  } else {
+    const float lo = fminf(mn, 0.f), hi = fmaxf(mx, 0.f);
+    // hi - lo rounded up to fp32 keeps the ceiling exact: the scale only moves up when
+    // the exact range lies above its fp32 rounding
+    float range = hi - lo;
+    if ((double)range < (double)hi - (double)lo) range = bits_f32(f32_bits(range) + 1u);
+    q.s = bf16_ceil_div(range, (float)levels);
+    q.z = q.s > 0.f ? (int)fminf(fmaxf(rne_quotient(-lo, q.s, 1.0f / q.s), 0.f), (float)levels) : 0;
+  }
+  q.r = q.s > 0.f ? 1.0f / q.s : 0.f;
+  return q;
+}
+
+// Stored code of x: round-half-even(x * r) + z, clipped to [lo, hi] (symmetric:
+// [1, 2^b - 1], asymmetric: [0, 2^b - 1]).  One fused multiply-add against the
+// constant 1.5 * 2^23 + z leaves the integer in the low mantissa bits (the product
+// x * r is exact inside the fma, so the only rounding is the final one); a clamp on the
+// bit pattern and a mask finish it.  Versus round-half-even(x / s) this can differ only
+// where x / s lies within a few fp32 ulps of a half-integer.
+__host__ __device__ inline int code_of(float x, float r, float magic, float lo, float hi) {
+  const float f = fminf(fmaxf(fmaf(x, r, magic), lo), hi);
+  return (int)(f32_bits(f) & 0xFFu);
+}
+
+struct CodeRange {
+  float magic, lo, hi;   // 1.5 * 2^23 + z and the clamp bounds in the same domain
+};
+
+__host__ __device__ inline CodeRange code_range(int z, bool asym, int bits) {
+  CodeRange c;
+  const float base = 12582912.0f;       // 1.5 * 2^23: bit pattern 0x4B400000
+  c.magic = base + (float)z;
+  c.lo = base + (asym ? 0.f : 1.f);
+  c.hi = base + (float)((1 << bits) - 1);
+  return c;
 }
 
 }  // namespace pace

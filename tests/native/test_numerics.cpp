@@ -48,6 +48,16 @@ int main() {
     EXPECT(bf16_ceil_from_f64(on) == want, "bf16_ceil on grid %.9g", want);
     n += 2;
   }
+  // bf16 ceiling of m / k computed in fp32 (the kernels' scale rule)
+  for (int i = 0; i < 300000; ++i) {
+    const float ks[4] = {7.f, 15.f, 127.f, 255.f};
+    const float k = ks[i & 3];
+    float m = (float)std::exp(U(rng) * 30.0);
+    if (i % 5 == 0) m = ref_bf16_ceil(std::exp(U(rng) * 20.0)) * k;   // exact multiples
+    const float got = bf16_ceil_div(m, k), want = ref_bf16_ceil((double)m / (double)k);
+    EXPECT(got == want, "bf16_ceil_div(%.9g, %g) = %.9g want %.9g", m, k, got, want);
+    n++;
+  }
   // exact RNE quotient, including constructed exact ties and near ties
   for (int i = 0; i < 400000; ++i) {
     float s = ref_bf16_ceil(std::exp(U(rng) * 10.0));
@@ -69,6 +79,41 @@ int main() {
     double got = rne_quotient(x, s, r), want = ref_rne_quot(x, s);
     EXPECT(got == want, "rne(%.9g / %.9g) = %g want %g", x, s, got, want);
     n++;
+  }
+  // magic-number code decision: rne(x * r) + z clipped, equal to the exact rne(x / s) + z
+  // except within a few fp32 ulps of a half-integer quotient
+  for (int i = 0; i < 300000; ++i) {
+    const bool asym = i & 1;
+    const int bits = (i & 2) ? 8 : 4;
+    float s = ref_bf16_ceil(std::exp(U(rng) * 8.0));
+    const int levels = (1 << bits) - 1, zsym = 1 << (bits - 1);
+    const int z = asym ? (int)(std::fabs(U(rng)) * levels) : zsym;
+    float x = (float)(U(rng) * (levels + 2) * (double)s);
+    CodeRange cr = code_range(z, asym, bits);
+    int got = code_of(x, 1.0f / s, cr.magic, cr.lo, cr.hi);
+    double q = (double)x / (double)s;
+    double want = ref_rne_quot(x, s) + z;
+    const double lo = asym ? 0 : 1, hi = levels;
+    want = want < lo ? lo : (want > hi ? hi : want);
+    const double frac = std::fabs(q - std::floor(q) - 0.5);
+    EXPECT(got == (int)want || frac < 1e-5, "code_of(%.9g, s=%.9g, z=%d, bits=%d) = %d want %g", x, s, z, bits, got, want);
+    n++;
+  }
+  // group parameters: zero group, symmetric and asymmetric ranges
+  {
+    GroupQuant g0 = group_quant(0.f, 0.f, false, 4);
+    EXPECT(g0.s == 0.f && g0.z == 8 && g0.r == 0.f, "zero sym group");
+    GroupQuant g1 = group_quant(0.f, 0.f, true, 4);
+    EXPECT(g1.s == 0.f && g1.z == 0, "zero asym group");
+    CodeRange cr = code_range(g0.z, false, 4);
+    EXPECT(code_of(1.5f, g0.r, cr.magic, cr.lo, cr.hi) == 8, "zero scale gives stored zero");
+    GroupQuant g2 = group_quant(-1.0f, 3.0f, false, 4);
+    EXPECT(g2.s == ref_bf16_ceil(3.0 / 7.0) && g2.z == 8, "sym scale");
+    GroupQuant g3 = group_quant(0.5f, 3.0f, true, 4);          // range forced to include 0
+    EXPECT(g3.s == ref_bf16_ceil(3.0 / 15.0) && g3.z == 0, "asym scale with lo clipped to 0");
+    GroupQuant g4 = group_quant(-2.0f, 1.0f, true, 4);
+    EXPECT(g4.s == ref_bf16_ceil(3.0 / 15.0) && g4.z == (int)ref_rne_quot(2.0f, g4.s), "asym zero point");
+    n += 6;
   }
   // bf16 round-to-nearest-even of fp32
   for (int i = 0; i < 100000; ++i) {
