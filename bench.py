@@ -12,13 +12,20 @@ pace_prefill_chunk before timing.
 
 One bench "step" = one decode period: dP tokens x L layers of pace_decode_step, i.e. every
 decode row of the path (append, dequantise, replay, output, fold, requantise) once per
-(layer, head, sequence).  A period is captured once in a HIP graph with an event pair
-around every launch; `--steps` replays are timed.  value = B * dP * steps / time.
+(layer, head, sequence).  A period is captured once in a HIP graph; `--warmup` replays are
+untimed, then `--steps` replays are timed between two events on the launch stream with a
+device synchronisation on both sides.  value = B * dP * steps / time.
 
 roofline: the decode kernel's algorithmic bytes per launch (state read 8704 B, buffered
 tokens read, q/k/v/a/beta in, append write, o out, and on flushing steps the 8704 B state
-write, per (sequence, head)) divided by its mean launch duration from the in-graph events.
-cpu_baseline: the fp64 oracle on a bounded sample of the same workload on the host.
+write, per (sequence, head)), averaged over the dP positions of a period, divided by the
+mean launch duration in the timed region (timed-region time / launches; the graph holds
+only decode launches).  traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE +
+WRITE_SIZE, scaled by the same counters on a copy of known size, read from the committed
+counter summary when it was taken on the current kernel source, else null.
+Also reported: a same-box copy ceiling, the bf16 per-token-state baseline on the same
+tokens, a batch sweep B = 1, 16, 32, 64, 128 (PACE-4 and bf16 at each), and
+cpu_baseline: the fp64 oracle on a bounded sample of the same workload on one host core.
 """
 from __future__ import annotations
 
@@ -55,6 +62,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--sweep", action="store_true", default=True)
+    ap.add_argument("--no-sweep", dest="sweep", action="store_false")
+    ap.add_argument("--sweep-batches", default="1,16,32,64,128")
     return ap.parse_args()
 
 
@@ -126,7 +136,10 @@ def algorithmic_bytes_per_launch(cfg, n0, L):
 
 def kernel_durations(torch, stream, calls, periods=2):
     """Mean GPU duration of each launch in `calls`, from event pairs recorded around it on
-    its stream.  Returns [periods, len(calls)] in ms."""
+    its stream, launched eagerly.  Every launch is enqueued behind a GPU spin first, so
+    the brackets hold GPU work only; an event pair adds its own overhead, so these
+    durations are an upper bound, used for the per-position (flush / no flush) split.
+    Returns [periods, len(calls)] in ms."""
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
           for _ in range(periods)]
     torch.cuda.synchronize()
@@ -141,36 +154,71 @@ def kernel_durations(torch, stream, calls, periods=2):
     return np.array([[s.elapsed_time(e) for s, e in row] for row in ev])
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build's path runs on a single MI355X and "
-              f"has no multi-GPU mode (asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import bit_recurrent_state_amd as pace
+def time_graph(torch, stream, calls, steps, warmup):
+    """Capture `calls` once in a HIP graph on `stream`; replay it `warmup` times untimed,
+    then `steps` times between two events on that stream, with a device synchronisation
+    on both sides.  Returns the timed milliseconds."""
+    with torch.cuda.stream(stream):
+        for c in calls:                      # warm the path once outside capture
+            c()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for c in calls:
+            c()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    del graph
+    return ms
 
-    torch.cuda.set_device(0)
-    B, Hv, Hk, d, dP, Lyr = args.batch, args.heads, args.kv_heads, args.dim, args.dP, args.layers
+
+def copy_ceiling(torch, nbytes=1 << 30, reps=5):
+    """Device-to-device copy of `nbytes` (torch's vectorised copy kernel): the same-box
+    streaming ceiling, counting read + write bytes."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (s.elapsed_time(e) / 1e3) / 1e9
+    del src, dst
+    return gbs
+
+
+def make_cfg(pace, args, B):
+    d, Hv, Hk, dP = args.dim, args.heads, args.kv_heads, args.dP
     if args.variant == "pace4":
-        cfg = pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP)
-    else:
-        # head map: a quarter of the heads at 8 bits (fixed map; the E_h ranking itself is
-        # exercised by pace_head_alloc in the tests)
-        hb = [8 if h % 4 == 0 else 4 for h in range(Hv)]
-        cfg = pace.pace48(hb, B=B, Hv=Hv, Hk=Hk, d=d, dP=dP, buf="int8" if args.variant == "pace48-int8" else "mixed")
-    L = pace.layout(cfg)
-    log(f"variant {args.variant} B={B} Hv={Hv} Hk={Hk} d={d} dP={dP} layers={Lyr} "
-        f"state/layer {L['state_bytes'] / 1e6:.1f} MB buffer/layer {L['buffer_bytes'] / 1e6:.1f} MB")
+        return pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP)
+    # head map: a quarter of the heads at 8 bits (a fixed map: any map with the same count
+    # moves the same bytes; the E_h ranking itself is pace_head_alloc's, tested separately)
+    hb = [8 if h % 4 == 0 else 4 for h in range(Hv)]
+    return pace.pace48(hb, B=B, Hv=Hv, Hk=Hk, d=d, dP=dP, buf="int8" if args.variant == "pace48-int8" else "mixed")
 
-    # ---- per-layer state, buffer, decode inputs; 512-token context by prefill
+
+def build_layers(torch, pace, args, cfg):
+    """Per layer: a zeroed state and buffer, the context written by pace_prefill_chunk,
+    and dP decode tokens."""
+    B, Hv, Hk, d, dP = cfg.B, cfg.Hv, cfg.Hk, cfg.dk, cfg.dP
+    L = pace.layout(cfg)
     layers = []
-    t0 = time.time()
-    for l in range(Lyr):
+    for l in range(args.layers):
         st = torch.zeros(L["state_bytes"], dtype=torch.uint8, device="cuda")
         bu = torch.zeros(L["buffer_bytes"], dtype=torch.uint8, device="cuda")
-        seed = 1000 * args.seed + l
-        ctx = make_layer_inputs(torch, B, args.context + dP, Hv, Hk, d, seed)
+        ctx = make_layer_inputs(torch, B, args.context + dP, Hv, Hk, d, 1000 * args.seed + l)
         o_ctx = torch.empty((B, args.context, Hv, d), dtype=torch.bfloat16, device="cuda")
         pq, pk_, pv, pa, pb = (x[:, :args.context].contiguous() for x in ctx)
         ws_n = pace.prefill_workspace_bytes(cfg, args.context)
@@ -181,63 +229,95 @@ def main():
         layers.append(dict(state=st, buf=bu, toks=toks, o=o))
         del ctx, o_ctx, pq, pk_, pv, pa, pb, ws
     torch.cuda.synchronize()
-    log(f"context prefilled in {time.time() - t0:.1f}s")
+    return layers, L
 
-    # ---- one decode period (dP tokens x L layers) as pre-marshalled calls
+
+def run_decode(torch, pace, args, B, steps, warmup, split=False):
+    """Decode periods of the L-layer stack at batch B.  Returns a dict of figures."""
+    cfg = make_cfg(pace, args, B)
+    dP, Lyr = cfg.dP, args.layers
+    t0 = time.time()
+    layers, L = build_layers(torch, pace, args, cfg)
     stream = torch.cuda.Stream()
     calls = []
     for t in range(dP):
         for ly in layers:
             q, k, v, a, b_ = ly["toks"][t]
             calls.append(pace.prepare_decode_step(cfg, ly["state"], ly["buf"], q, k, v, a, b_, ly["o"], stream=stream))
-    n_launch = len(calls)
-    with torch.cuda.stream(stream):
-        for c in calls:                      # warm the path once outside capture
-            c()
-    stream.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for c in calls:
-            c()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-
-    # timed region: graph replays
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    with torch.cuda.stream(stream):
-        for _ in range(args.steps):
-            graph.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    tokens_per_s = B * dP * args.steps / (total_ms / 1e3)
-
-    # per-launch kernel durations: the same period launched eagerly on the same stream,
-    # each launch between two events; every launch is enqueued behind a GPU spin first,
-    # so the brackets hold GPU work only
-    kern_ms = kernel_durations(torch, stream, calls, periods=2)
-    # roofline of the decode kernel: algorithmic bytes / mean launch duration
+    ms = time_graph(torch, stream, calls, steps, warmup)
+    n_launch = len(calls) * steps
+    launch_s = ms / 1e3 / n_launch                       # mean launch duration in the timed region
     per_pos = np.array([algorithmic_bytes_per_launch(cfg, t, L) for t in range(dP)])
     bytes_per_launch = float(per_pos.mean())
-    kern_ms = kern_ms.mean(axis=0)
-    mean_kern_s = float(kern_ms.mean()) / 1e3
-    achieved = bytes_per_launch / mean_kern_s / 1e9
-    stream_gbs = bytes_per_launch * n_launch * args.steps / (total_ms / 1e3) / 1e9
-    log(f"decode: {tokens_per_s:,.0f} tok/s, {ms_per_step:.3f} ms/period, kernel mean {kern_ms.mean() * 1e3:.2f} us "
-        f"(flush step {kern_ms.reshape(dP, Lyr)[-1].mean() * 1e3:.2f} us), {achieved:.0f} GB/s in-kernel, "
-        f"{stream_gbs:.0f} GB/s over the timed region")
+    res = dict(cfg=cfg, L=L, B=B, ms=ms, ms_per_step=ms / steps,
+               tokens_per_s=B * dP * steps / (ms / 1e3),
+               bytes_per_launch=bytes_per_launch, launch_us=launch_s * 1e6,
+               achieved=bytes_per_launch / launch_s / 1e9,
+               setup_s=time.time() - t0)
+    if split:
+        kern = kernel_durations(torch, stream, calls, periods=2).mean(axis=0).reshape(dP, Lyr)
+        res["eager_us"] = float(kern.mean() * 1e3)
+        res["eager_flush_us"] = float(kern[-1].mean() * 1e3)
+        res["eager_noflush_us"] = float(kern[:-1].mean() * 1e3)
+    res["layers"] = layers
+    return res
+
+
+def decode_traffic(cfg_name):
+    """HBM traffic per launch of the decode kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source (sha256 recorded with it)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_traffic_{cfg_name}.txt")
+    src = os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", "pace_decode.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the PACE decode path here runs on a single MI355X "
+              f"and has no multi-GPU mode (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_recurrent_state_amd as pace
+
+    torch.cuda.set_device(0)
+    B, Hv, Hk, d, dP, Lyr = args.batch, args.heads, args.kv_heads, args.dim, args.dP, args.layers
+    cfg0 = make_cfg(pace, args, B)
+    L0 = pace.layout(cfg0)
+    log(f"variant {args.variant} B={B} Hv={Hv} Hk={Hk} d={d} dP={dP} layers={Lyr} "
+        f"state/layer {L0['state_bytes'] / 1e6:.1f} MB buffer/layer {L0['buffer_bytes'] / 1e6:.1f} MB")
+
+    r = run_decode(torch, pace, args, B, args.steps, args.warmup, split=True)
+    log(f"decode: {r['tokens_per_s']:,.0f} tok/s, {r['ms_per_step']:.3f} ms/period, {r['launch_us']:.2f} us "
+        f"per launch in the graph = {r['achieved']:.0f} GB/s; eager brackets: {r['eager_noflush_us']:.2f} us "
+        f"without flush, {r['eager_flush_us']:.2f} us with (setup {r['setup_s']:.1f}s)")
+    cfg, layers = r["cfg"], r.pop("layers")
+    ceiling = copy_ceiling(torch)
+    log(f"copy ceiling {ceiling:.0f} GB/s")
+    traffic = decode_traffic(args.variant + f"_b{B}") if args.variant == "pace4" else None
 
     result = {
         "metric": "decode tokens/s & achieved HBM GB/s (% peak), int4 state dP=8, B=1..128",
-        "value": round(tokens_per_s, 1),
+        "value": round(r["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -247,27 +327,54 @@ def main():
                                f"({Hk} key heads), d={d}, B={B}, dP={dP}, {args.context}-token context; "
                                f"step = one decode period ({dP} tokens x {Lyr} layers)",
                    "global_batch": B, "seq_len": args.context, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel<128,1,0,1>", "bytes_per_launch": round(bytes_per_launch),
-                     "mean_launch_us": round(kern_ms.mean() * 1e3, 3),
-                     "timed_region_GBps": round(stream_gbs, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": "pace decode_kernel (pace_decode_step)",
+                     "bytes_per_launch": round(r["bytes_per_launch"]),
+                     "mean_launch_us": round(r["launch_us"], 3),
+                     "eager_launch_us": {"no_flush": round(r["eager_noflush_us"], 3),
+                                         "flush": round(r["eager_flush_us"], 3)},
+                     "copy_ceiling_GBps": round(ceiling, 1),
+                     "frac_of_copy_ceiling": round(r["achieved"] / ceiling, 4)},
     }
 
     # ---- bf16 per-token-state baseline on the same shape
     if args.baseline:
-        try:
-            result["bf16_baseline"] = run_bf16_baseline(torch, pace, args, cfg, layers)
-        except Exception as e:  # noqa: BLE001
-            result["bf16_baseline"] = {"error": repr(e)}
+        result["bf16_baseline"] = run_bf16_baseline(torch, pace, args, cfg, layers)
     del layers
+    torch.cuda.empty_cache()
+
+    # ---- batch sweep (PACE-4 and the bf16 baseline at each B)
+    if args.sweep:
+        sweep = []
+        for Bs in [int(x) for x in args.sweep_batches.split(",")]:
+            rs = run_decode(torch, pace, args, Bs, max(3, args.steps // 2), 2)
+            ent = {"B": Bs, "tokens_per_s": round(rs["tokens_per_s"], 1), "GBps": round(rs["achieved"], 1),
+                   "mean_launch_us": round(rs["launch_us"], 3),
+                   "working_set_MB": round((rs["L"]["state_bytes"] + rs["L"]["buffer_bytes"]) * Lyr / 1e6, 1)}
+            if args.baseline:
+                bl = run_bf16_baseline(torch, pace, args, rs["cfg"], rs["layers"], steps=max(3, args.steps // 2),
+                                       warmup=2, split=False)
+                ent["bf16_tokens_per_s"] = bl["value"]
+                ent["bf16_GBps"] = bl["timed_region_GBps"]
+                ent["speedup_vs_bf16"] = round(rs["tokens_per_s"] / bl["value"], 3)
+            del rs["layers"]
+            torch.cuda.empty_cache()
+            log(f"sweep B={Bs}: {ent}")
+            sweep.append(ent)
+        result["batch_sweep"] = sweep
     torch.cuda.synchronize()
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, Hv * Lyr)
     print(json.dumps(result), flush=True)
 
 
-def run_bf16_baseline(torch, pace, args, cfg, layers):
+def run_bf16_baseline(torch, pace, args, cfg, layers, steps=None, warmup=None, split=True):
+    """The bf16 per-token-state decode (pace_bf16_decode_step) over the same tokens:
+    read S, update, write S every token."""
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     B, Hv, Hk, d, dP, Lyr = cfg.B, cfg.Hv, cfg.Hk, cfg.dk, cfg.dP, args.layers
     bcfg = pace.LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=cfg.group, bf16_io=True, dP=dP)
     states = [torch.randn((B, Hv, d, d), device="cuda").mul_(0.05).to(torch.bfloat16) for _ in range(Lyr)]
@@ -277,36 +384,21 @@ def run_bf16_baseline(torch, pace, args, cfg, layers):
         for l, ly in enumerate(layers):
             q, k, v, a, b_ = ly["toks"][t]
             calls.append(pace.prepare_bf16_decode_step(bcfg, states[l], q, k, v, a, b_, ly["o"], stream=stream))
-    with torch.cuda.stream(stream):
-        for c in calls:
-            c()
-    stream.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for c in calls:
-            c()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record(stream)
-    with torch.cuda.stream(stream):
-        for _ in range(args.steps):
-            graph.replay()
-    e.record(stream)
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e)
-    tps = B * dP * args.steps / (ms / 1e3)
+    ms = time_graph(torch, stream, calls, steps, warmup)
+    tps = B * dP * steps / (ms / 1e3)
     per_launch = B * Hv * (2 * d * d * 2 + (2 * d * 2) / (Hv // Hk) + 2 * d * 2 + 8)
-    gbs = per_launch * dP * Lyr * args.steps / (ms / 1e3) / 1e9
-    kms = kernel_durations(torch, stream, calls, periods=1).mean(axis=0)
-    kgbs = per_launch / (kms.mean() / 1e3) / 1e9
-    log(f"bf16 per-token baseline: {tps:,.0f} tok/s, {gbs:.0f} GB/s over the timed region, "
-        f"kernel mean {kms.mean() * 1e3:.2f} us = {kgbs:.0f} GB/s in-kernel")
+    launch_us = ms * 1e3 / (len(calls) * steps)
+    gbs = per_launch / (launch_us / 1e6) / 1e9
+    out = {"value": round(tps, 1), "unit": "tokens/s", "timed_region_GBps": round(gbs, 1),
+           "bytes_per_launch": per_launch, "mean_launch_us": round(launch_us, 3)}
+    msg = f"bf16 per-token baseline B={B}: {tps:,.0f} tok/s, {launch_us:.2f} us per launch = {gbs:.0f} GB/s"
+    if split:
+        kms = kernel_durations(torch, stream, calls, periods=1).mean()
+        out["eager_launch_us"] = round(float(kms) * 1e3, 3)
+        msg += f" (eager bracket {kms * 1e3:.2f} us)"
+    log(msg)
     del states
-    return {"value": round(tps, 1), "unit": "tokens/s", "timed_region_GBps": round(gbs, 1),
-            "bytes_per_launch": per_launch, "mean_launch_us": round(float(kms.mean()) * 1e3, 3),
-            "in_kernel_GBps": round(kgbs, 1)}
+    return out
 
 
 def cpu_baseline(args, tiles_per_token):
@@ -323,14 +415,16 @@ def cpu_baseline(args, tiles_per_token):
     bu = pk.pack_buffer(ocfg, random_buffer_parts(6, Bs, Hv, Hk, d, d, dP, False, counts=[0] * Bs))
     toks = make_tokens(7, Bs, 64, Hv, Hk, d, d, bf16=True)
     tiles = [(b, h) for b in range(Bs) for h in range(0, Hv, 4)]
-    t0 = time.time()
-    steps = 0
-    while True:
-        o, st, bu, _ = pk.decode_step_layer(ocfg, st, bu, *toks.token(steps % 64), tiles=tiles)
-        steps += 1
-        if time.time() - t0 > args.cpu_seconds and steps % dP == 0:
-            break
-    el = time.time() - t0
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):               # one host thread: the figure is per core
+        t0 = time.time()
+        steps = 0
+        while True:
+            o, st, bu, _ = pk.decode_step_layer(ocfg, st, bu, *toks.token(steps % 64), tiles=tiles)
+            steps += 1
+            if time.time() - t0 > args.cpu_seconds and steps % dP == 0:
+                break
+        el = time.time() - t0
     tile_steps = steps * len(tiles)
     threads = os.environ.get("OMP_NUM_THREADS", "unset")
     try:
@@ -341,7 +435,7 @@ def cpu_baseline(args, tiles_per_token):
             "kind": "oracle",
             "sample": f"{tile_steps} tile-steps ({len(tiles)} (seq, head) tiles x {steps} decode steps incl. "
                       f"{steps // dP} flushes) of the PACE-4 layer shape in {el:.1f}s, single-threaded "
-                      f"Python/NumPy fp64; tokens/s = tile-steps/s / ({tiles_per_token} tiles per token); "
+                      f"Python/NumPy fp64 (BLAS limited to 1 thread); tokens/s = tile-steps/s / ({tiles_per_token} tiles per token); "
                       f"host affinity {cores} cores, OMP_NUM_THREADS={threads}"}
 
 
