@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--sweep", action="store_true", default=True)
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
     ap.add_argument("--sweep-batches", default="1,16,32,64,128")
+    ap.add_argument("--prefill", action="store_true", default=True)
+    ap.add_argument("--no-prefill", dest="prefill", action="store_false")
+    ap.add_argument("--prefill-tokens", type=int, default=32768)
+    ap.add_argument("--prefill-reps", type=int, default=3)
     return ap.parse_args()
 
 
@@ -263,6 +267,84 @@ def run_decode(torch, pace, args, B, steps, warmup, split=False):
     return res
 
 
+PREFILL_MFMA_PEAK_TFLOPS = 157.3          # MI355X dense fp32 matrix peak
+
+
+def prefill_flops(T, Hv, B, d, chunk=256, sb=64):
+    """(algorithmic, executed) flops of pace_prefill_chunk over B x Hv (sequence, head)
+    pairs of T tokens.  Algorithmic: the WY form on whole 256-token chunks (72.7 MFLOP per
+    chunk-head at d = 128); executed: the fp32 MFMA work the 64-token sub-block kernel
+    issues (16x16x4 MFMAs, 2048 flops each)."""
+    C = chunk
+    # MACs with triangularity: K K^T and Q K^T (half), W_v and W_k (T lower), P U (half),
+    # U, Q S_0, S_C (full), the unit-triangular inverse (C^3 / 6); 2 flops per MAC
+    per_chunk = 2 * (2.5 * C * C * d + 3 * C * d * d + C ** 3 / 6)
+    n_chunks = -(-T // C)
+    alg = per_chunk * n_chunks * B * Hv
+    tt = sb // 16
+    kt = d // 16
+    pairs = tt * (tt + 1) // 2
+    mfma_per_sb = (2 * pairs * (d // 4)          # Gram and query-key tiles
+                   + tt * (d // 16) * 4 * (d // 16)    # K S (all column tiles)
+                   + tt * kt * 4 * (d // 16)           # Q S
+                   + pairs * 4 * (d // 16)             # P U
+                   + tt * 4 * kt * (d // 16))          # S update
+    n_sb = -(-T // sb)
+    executed = mfma_per_sb * 2 * 16 * 16 * 4 * n_sb * B * Hv
+    return alg, executed
+
+
+def run_long_prefill(torch, pace, args):
+    """Long chunked prefill: B = 4 sequences x 32,768 tokens, 32 value / 16 key heads,
+    d = 128, bf16 q/k/v, fp32 gates, int4 g = 64 rounded once per 256-token chunk; then
+    decode steps of that layer at dP = 8 (B = 4 under-fills the chip; reported only)."""
+    B, T, Hv, Hk, d = 4, args.prefill_tokens, args.heads, args.kv_heads, args.dim
+    cfg = pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=args.dP)
+    L = pace.layout(cfg)
+    q, k, v, a, beta = make_layer_inputs(torch, B, T + 8 * args.dP, Hv, Hk, d, 4000 + args.seed, timeline=T + 8 * args.dP)
+    pq, pk_, pv, pa, pb = (x[:, :T].contiguous() for x in (q, k, v, a, beta))
+    o = torch.empty((B, T, Hv, d), dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros(L["state_bytes"], dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    call = pace.prepare_prefill_chunk(cfg, st, pq, pk_, pv, pa, pb, o, stream=stream)
+    times = []
+    for rep in range(1 + args.prefill_reps):
+        st.zero_()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        with torch.cuda.stream(stream):
+            call()
+        e.record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            times.append(s.elapsed_time(e))
+    ms = float(np.median(times))
+    alg, exe = prefill_flops(T, Hv, B, d)
+    res = {"workload": f"long chunked prefill B={B} x {T} tokens, {Hv} value / {Hk} key heads, d={d}, bf16 io, "
+                       f"int4 g=64 rounded per 256-token chunk",
+           "ms": round(ms, 3), "tokens_per_s": round(B * T / (ms / 1e3), 1),
+           "algorithmic_TFLOP": round(alg / 1e12, 4), "algorithmic_TFLOPs": round(alg / (ms / 1e3) / 1e12, 2),
+           "executed_mfma_TFLOP": round(exe / 1e12, 4), "executed_TFLOPs": round(exe / (ms / 1e3) / 1e12, 2),
+           "mfma_dtype": "fp32 (v_mfma_f32_16x16x4_f32)", "mfma_peak_TFLOPs": PREFILL_MFMA_PEAK_TFLOPS,
+           "mfma_util": round(exe / (ms / 1e3) / 1e12 / PREFILL_MFMA_PEAK_TFLOPS, 4),
+           "workgroups": B * Hv}
+    log(f"long prefill: {ms:.2f} ms, {res['tokens_per_s']:,.0f} tok/s, executed {res['executed_TFLOPs']} TFLOP/s "
+        f"(util {res['mfma_util']:.3f} of fp32 MFMA peak), algorithmic {res['algorithmic_TFLOPs']} TFLOP/s")
+    # decode after the prompt: B = 4, one layer
+    bu = torch.zeros(L["buffer_bytes"], dtype=torch.uint8, device="cuda")
+    od = torch.empty((B, Hv, d), dtype=torch.bfloat16, device="cuda")
+    toks = [tuple(x[:, T + t].contiguous() for x in (q, k, v, a, beta)) for t in range(8 * args.dP)]
+    calls = [pace.prepare_decode_step(cfg, st, bu, *tk, od, stream=stream) for tk in toks]
+    dms = time_graph(torch, stream, calls, max(2, args.steps // 4), 1)
+    n = len(calls) * max(2, args.steps // 4)
+    res["decode_after_prefill"] = {"B": B, "layers": 1, "tokens_per_s_per_layer": round(B * n / (dms / 1e3), 1),
+                                   "mean_launch_us": round(dms * 1e3 / n, 3)}
+    del q, k, v, a, beta, pq, pk_, pv, pa, pb, o, st, bu
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_traffic(cfg_name):
     """HBM traffic per launch of the decode kernel from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source (sha256 recorded with it)."""
@@ -364,6 +446,8 @@ def main():
             log(f"sweep B={Bs}: {ent}")
             sweep.append(ent)
         result["batch_sweep"] = sweep
+    if args.prefill:
+        result["long_prefill"] = run_long_prefill(torch, pace, args)
     torch.cuda.synchronize()
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, Hv * Lyr)

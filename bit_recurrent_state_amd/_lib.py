@@ -214,6 +214,31 @@ def prefill_chunk(cfg: LayerConfig, state, q, k, v, a, beta, o, workspace=None, 
     _check(st, "pace_prefill_chunk")
 
 
+def prepare_prefill_chunk(cfg: LayerConfig, state, q, k, v, a, beta, o, workspace=None, stream=None):
+    """Pre-marshalled pace_prefill_chunk (see prepare_decode_step)."""
+    import torch
+    T = a.shape[1]
+    L = layout(cfg)
+    io = _io(cfg)
+    c = cfg._c()
+    need = prefill_workspace_bytes(cfg, T)
+    ws = _ptr(workspace, "workspace", torch.uint8, optional=need == 0)
+    wsb = workspace.numel() if workspace is not None else 0
+    args = (ctypes.byref(c), _ptr(state, "state", torch.uint8, L["state_bytes"]),
+            _ptr(q, "q", io, cfg.B * T * cfg.Hk * cfg.dk), _ptr(k, "k", io, cfg.B * T * cfg.Hk * cfg.dk),
+            _ptr(v, "v", io, cfg.B * T * cfg.Hv * cfg.dv), _ptr(a, "a", torch.float32, cfg.B * T * cfg.Hv),
+            _ptr(beta, "beta", torch.float32, cfg.B * T * cfg.Hv), T,
+            _ptr(o, "o", io, cfg.B * T * cfg.Hv * cfg.dv), ws, wsb, _stream(stream))
+    fn = LIB.pace_prefill_chunk
+
+    def call():
+        st = fn(*args)
+        if st != PACE_OK:
+            raise PaceError(st, "pace_prefill_chunk")
+    call._keep = (c, args)
+    return call
+
+
 def bf16_decode_step(cfg: LayerConfig, state, q, k, v, a, beta, o, stream=None):
     """pace_bf16_decode_step; state bf16 [B, Hv, dv, dk]."""
     import torch

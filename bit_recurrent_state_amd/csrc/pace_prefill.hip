@@ -2,11 +2,25 @@
 // the prefill rounding period equals the chunk kernel's chunk length, 256 tokens; news
 // item "Two observations": chunked prefill writes the state once per chunk).
 //
-// This kernel runs the exact recurrence token by token inside each chunk with the
-// unrounded fp32 state held in registers, emits o_t from the post-update state, and
-// requantises the state into the packed record after every `chunk` tokens and after the
-// last token.  One workgroup (4 waves) per (sequence, value head); D/8 lanes share a
-// value column, each holding 8 consecutive keys.
+// WY form of the gated delta rule (review, "1. Key Terms & Definitions": u_t =
+// beta_t (v_t - a_t S^T k_t), S_t = a_t S + k_t u_t^T), applied to sub-blocks of 64
+// tokens with the state kept unrounded in fp32 between sub-blocks and rounded only at
+// chunk boundaries and after the call's last token.  For a sub-block with cumulative
+// log-decays g_t (Gamma_t = e^{g_t}) and starting state S:
+//   A = strictly lower [beta_t e^{g_t - g_i} k_t . k_i]
+//   (I + A) U = diag(beta) V - diag(beta Gamma) K S                   (forward solve)
+//   O = diag(Gamma) Q S + (lower-incl [e^{g_t - g_i} q_t . k_i]) U
+//   S' = Gamma_end S + K^T diag(e^{g_end - g}) U
+// which is the token loop's result exactly in real arithmetic.  Every contraction runs on
+// v_mfma_f32_16x16x4_f32 (fp32 operands, fp32 accumulation: the state must stay accurate
+// to ~1e-5 relative for the rounding decisions at the chunk end).
+//
+// One workgroup (4 wave64s) per (sequence, value head).  The state S lives in the MFMA
+// accumulators for the whole call: wave w owns value columns [w D/4, (w+1) D/4), all keys;
+// lane l of a 16x16 accumulator tile holds rows 4(l/16)+r, column l%16.  Contractions over
+// keys use those accumulators directly as the B operand, pairing them with an A operand
+// read in the matching (permuted) key order.  The next sub-block's inputs are prefetched
+// into registers while the current one is computed.
 #include <hip/hip_runtime.h>
 
 #include "pace_internal.h"
@@ -15,186 +29,429 @@
 namespace pace {
 namespace {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
+constexpr int kSB = 64;              // tokens per sub-block
 
-template <int LPC>
-__device__ inline float seg_sum(float x) {
-#pragma unroll
-  for (int o = LPC / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-__device__ inline float seg_max(float x, int width) {
-  for (int o = width / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ inline float seg_min(float x, int width) {
-  for (int o = width / 2; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
-  return x;
-}
-
-template <bool BF16>
-__device__ inline float ld(const void* p, size_t i) {
-  if constexpr (BF16) return bf16_to_f32(((const uint16_t*)p)[i]);
-  else return ((const float*)p)[i];
+__device__ inline v4f mfma4(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 struct Rec {
   uint8_t* base;
   uint16_t* scales;
   uint8_t* zeros;
-  int bits, NG, group, asym;
+  int bits, NG, asym;
 };
 
 // Packed-record position of the 8 keys 8m..8m+7 of column j: the unit u whose base key
 // is 8m, i.e. u = (m mod 4) * (D/32) + m / 4.
 template <int D>
 __device__ inline uint8_t* unit_ptr(const Rec& r, int j, int m) {
-  const int KB = D / 32;
+  constexpr int KB = D / 32;
   const int u = (m & 3) * KB + (m >> 2);
   return r.base + (size_t)j * (D * r.bits / 8) + u * r.bits;
 }
 
 template <int D>
-__device__ inline void dequant_unit(const Rec& r, int j, int m, float x[8]) {
-  const uint8_t* up = unit_ptr<D>(r, j, m);
-  const int G = (8 * m) / r.group;
-  const float s = bf16_to_f32(r.scales[j * r.NG + G]);
-  int z;
-  if (r.asym) {
-    const int e = j * r.NG + G;
-    z = r.bits == 8 ? (int)r.zeros[e] : (int)((r.zeros[e >> 1] >> (4 * (e & 1))) & 15);
-  } else {
-    z = 1 << (r.bits - 1);
-  }
+__device__ inline void store_codes4(const Rec& r, int j, int kt, int qd, uint32_t c4) {
+  uint8_t* up = unit_ptr<D>(r, j, 2 * kt + (qd >> 1));
   if (r.bits == 4) {
-    const uint32_t d = *(const uint32_t*)up;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = s * (float)((int)((d >> (8 * (e & 3) + 4 * (e >> 2))) & 15) - z);
+    const uint32_t hi = __shfl_xor(c4, 16);          // keys 8m + 4 .. 8m + 7 (lane group qd ^ 1)
+    if ((qd & 1) == 0) *(uint32_t*)up = c4 | (hi << 4);
   } else {
-    const uint2 d = *(const uint2*)up;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w = e < 4 ? d.x : d.y;
-      x[e] = s * (float)((int)((w >> (8 * (e & 3))) & 255) - z);
-    }
+    *(uint32_t*)(up + 4 * (qd & 1)) = c4;
   }
 }
 
-// Requantise the lane's 8 keys of column j (group of g/8 lanes), write codes, scale and
-// zero point, and replace x by its dequantised value.
-template <int D>
-__device__ inline void requant_unit(const Rec& r, int j, int m, float x[8]) {
-  const int width = r.group / 8;       // lanes per group
-  float mx = x[0], mn = x[0];
+// Round the accumulator state of one column tile to the packed record (and replace it by
+// its dequantised value), groups of GS keys.  Column j of this lane; lane group qd.
+template <int D, int GS>
+__device__ inline void requant_tile(v4f (&S)[D / 16], const Rec& r, int j, int qd) {
+  constexpr int KPG = GS / 16;         // key tiles per group
+  constexpr int NG = D / GS;
+  int zprev = 0;
 #pragma unroll
-  for (int e = 1; e < 8; ++e) { mx = fmaxf(mx, x[e]); mn = fminf(mn, x[e]); }
-  mx = seg_max(mx, width);
-  mn = seg_min(mn, width);
-  const int levels = (1 << r.bits) - 1, zsym = 1 << (r.bits - 1);
-  const float qmax = (float)(zsym - 1);
-  float sn;
-  int z;
-  if (!r.asym) {
-    sn = bf16_ceil_from_f64((double)fmaxf(fabsf(mx), fabsf(mn)) / (double)qmax);
-    z = zsym;
-  } else {
-    const float lo = fminf(mn, 0.f), hi = fmaxf(mx, 0.f);
-    sn = bf16_ceil_from_f64(((double)hi - (double)lo) / (double)levels);
-    z = sn > 0.f ? (int)fminf(fmaxf(rne_quotient(-lo, sn, 1.f / sn), 0.f), (float)levels) : 0;
-  }
-  const float rcp = sn > 0.f ? 1.f / sn : 0.f;
-  int code[8];
+  for (int G = 0; G < NG; ++G) {
+    float mx = S[G * KPG][0], mn = S[G * KPG][0];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if (sn == 0.f) code[e] = r.asym ? 0 : zsym;
-    else if (!r.asym) code[e] = (int)fminf(fmaxf(rne_quotient(x[e], sn, rcp), -qmax), qmax) + zsym;
-    else code[e] = (int)fminf(fmaxf(rne_quotient(x[e], sn, rcp) + (float)z, 0.f), (float)levels);
-    x[e] = sn * (float)(code[e] - z);
-  }
-  uint8_t* up = unit_ptr<D>(r, j, m);
-  if (r.bits == 4) {
-    uint32_t d = 0;
+    for (int kk = 0; kk < KPG; ++kk)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d |= (uint32_t)code[e] << (8 * (e & 3) + 4 * (e >> 2));
-    *(uint32_t*)up = d;
-  } else {
-    uint32_t d0 = 0, d1 = 0;
+      for (int i = 0; i < 4; ++i) { mx = fmaxf(mx, S[G * KPG + kk][i]); mn = fminf(mn, S[G * KPG + kk][i]); }
+    mx = fmaxf(mx, __shfl_xor(mx, 16)); mn = fminf(mn, __shfl_xor(mn, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)); mn = fminf(mn, __shfl_xor(mn, 32));
+    const GroupQuant gq = group_quant(mn, mx, r.asym != 0, r.bits);
+    const CodeRange cr = code_range(gq.z, r.asym != 0, r.bits);
+    const float fz = (float)gq.z;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { d0 |= (uint32_t)code[e] << (8 * e); d1 |= (uint32_t)code[e + 4] << (8 * e); }
-    *(uint2*)up = make_uint2(d0, d1);
-  }
-  const int G = (8 * m) / r.group;
-  const int zn = __shfl_down(z, width, 64);     // zero point of group G+1 (next lanes)
-  if (m % width == 0) {
-    r.scales[j * r.NG + G] = (uint16_t)(f32_bits(sn) >> 16);
-    if (r.asym) {
-      const int e = j * r.NG + G;
-      if (r.bits == 8) r.zeros[e] = (uint8_t)z;
-      else if ((e & 1) == 0) r.zeros[e >> 1] = (uint8_t)(z | (zn << 4));
+    for (int kk = 0; kk < KPG; ++kk) {
+      const int kt = G * KPG + kk;
+      uint32_t c4 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = code_of(S[kt][i], gq.r, cr.magic, cr.lo, cr.hi);
+        c4 |= (uint32_t)c << (8 * i);
+        S[kt][i] = gq.s * ((float)c - fz);
+      }
+      store_codes4<D>(r, j, kt, qd, c4);
     }
+    if (qd == 0) {
+      const int e = j * NG + G;
+      r.scales[e] = (uint16_t)(f32_bits(gq.s) >> 16);
+      if (r.asym) {
+        if (r.bits == 8) r.zeros[e] = (uint8_t)gq.z;
+        else if (G & 1) r.zeros[e >> 1] = (uint8_t)(zprev | (gq.z << 4));
+      }
+    }
+    zprev = gq.z;
   }
 }
 
 template <int D, int IO>
-__global__ __launch_bounds__(kThreads) void prefill_seq_kernel(PrefillParams p) {
-  constexpr int LPC = D / 8;
-  constexpr int CPW = 64 / LPC;
-  constexpr int CPB = CPW * (kThreads / 64);
-  constexpr int PASSES = D / CPB;
-  constexpr bool kBf16 = IO == 1;
+struct Inputs {
+  // raw 16-byte vectors of one sub-block: K, Q rows of the key head, V rows of the head
+  static constexpr int ES = IO == 1 ? 2 : 4;                 // element bytes
+  static constexpr int VPR = D * ES / 16;                    // vectors per row
+  static constexpr int NV = kSB * VPR / kThreads;            // vectors per thread per tensor
+  uint4 k[NV], q[NV], v[NV];
+  float a, beta;
+};
+
+template <int D, int IO>
+__device__ inline void load_inputs(Inputs<D, IO>& in, const PrefillParams& p, int b, int h, int kh,
+                                   int t0, int nt, int tid) {
+  using I = Inputs<D, IO>;
+#pragma unroll
+  for (int it = 0; it < I::NV; ++it) {
+    const int i = tid + it * kThreads;
+    const int t = i / I::VPR, c = i % I::VPR;
+    if (t < nt) {
+      const size_t kq = (((size_t)b * p.T + t0 + t) * p.Hk + kh) * (size_t)(D * I::ES) + 16 * c;
+      const size_t vo = (((size_t)b * p.T + t0 + t) * p.Hv + h) * (size_t)(D * I::ES) + 16 * c;
+      in.k[it] = *(const uint4*)((const uint8_t*)p.k + kq);
+      in.q[it] = *(const uint4*)((const uint8_t*)p.q + kq);
+      in.v[it] = *(const uint4*)((const uint8_t*)p.v + vo);
+    } else {
+      in.k[it] = in.q[it] = in.v[it] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  if (tid < kSB) {
+    const bool ok = tid < nt;
+    const size_t gi = ((size_t)b * p.T + t0 + (ok ? tid : 0)) * p.Hv + h;
+    in.a = ok ? p.a[gi] : 1.f;           // padding tokens: no decay, no write
+    in.beta = ok ? p.beta[gi] : 0.f;
+  }
+}
+
+template <int IO>
+__device__ inline void put8(float* dst, uint4 w) {
+  if constexpr (IO == 1) {
+    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f[2 * e] = bits_f32(x[e] << 16); f[2 * e + 1] = bits_f32(x[e] & 0xFFFF0000u); }
+    *(float4*)dst = make_float4(f[0], f[1], f[2], f[3]);
+    *(float4*)(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  } else {
+    *(float4*)dst = make_float4(bits_f32(w.x), bits_f32(w.y), bits_f32(w.z), bits_f32(w.w));
+  }
+}
+
+template <int D>
+struct Smem {
+  static constexpr int LD = D + 4;     // row stride of token-major tiles (floats)
+  static constexpr int LA = kSB + 4;
+  float K[kSB][LD];                    // keys of the sub-block
+  float Q[kSB][LD];                    // queries
+  float U[kSB][LD];                    // values, then right-hand sides, then U
+  float A[kSB][LA];                    // beta_t e^{g_t-g_i} k_t.k_i, strictly lower
+  float P[kSB][LA];                    // e^{g_t-g_i} q_t.k_i, lower incl. diagonal
+  float g[kSB];                        // cumulative log decay
+  float beta[kSB];
+};
+
+template <int D, int IO>
+__global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
+  constexpr int KT = D / 16;           // key tiles
+  constexpr int CT = D / 64;           // column tiles per wave
+  constexpr int TT = kSB / 16;         // token tiles
+  constexpr int VS = IO == 1 ? 8 : 4;  // floats per 16-byte input vector
+  using I = Inputs<D, IO>;
+  __shared__ Smem<D> sm;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, qd = lane >> 4;
   const int b = blockIdx.x / p.Hv, h = blockIdx.x % p.Hv, kh = h / p.gamma;
-  const int m = lane % LPC;
 
   const bool is8 = (p.mask8 >> h) & 1ull;
   const uint64_t below = h ? (p.mask8 & ((1ull << h) - 1ull)) : 0ull;
   const uint64_t n8 = (uint64_t)__popcll(below);
-  Rec r;
-  r.base = p.state + (uint64_t)b * p.seq_stride + (uint64_t)h * p.rec4 + n8 * (p.rec8 - p.rec4);
-  r.scales = (uint16_t*)(r.base + (is8 ? p.scales_off8 : p.scales_off4));
-  r.zeros = r.base + (is8 ? p.zeros_off8 : p.zeros_off4);
-  r.bits = is8 ? 8 : 4;
-  r.NG = D / p.group;
-  r.group = p.group;
-  r.asym = p.asym;
+  Rec rec;
+  rec.base = p.state + (uint64_t)b * p.seq_stride + (uint64_t)h * p.rec4 + n8 * (p.rec8 - p.rec4);
+  rec.scales = (uint16_t*)(rec.base + (is8 ? p.scales_off8 : p.scales_off4));
+  rec.zeros = rec.base + (is8 ? p.zeros_off8 : p.zeros_off4);
+  rec.bits = is8 ? 8 : 4;
+  rec.NG = D / p.group;
+  rec.asym = p.asym;
 
-  float S[PASSES][8];
+  // ---- initial state: dequantise this lane's accumulator entries (all loads first,
+  // branch-free: symmetric records read their scales in place of zero points)
+  v4f S[CT][KT];
+  {
+    uint32_t c4[CT][KT];
+    uint16_t sc[CT][KT];
+    uint8_t zb[CT][KT];
+    const int ub = rec.bits;                         // bytes per 8-key unit
+    const int sel8 = is8 ? 4 * (qd & 1) : 0;
+    const uint8_t* zsrc = p.asym ? rec.zeros : (const uint8_t*)rec.scales;
 #pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass) {
-    const int j = pass * CPB + wave * CPW + lane / LPC;
-    dequant_unit<D>(r, j, m, S[pass]);
-  }
-  for (int t = 0; t < p.T; ++t) {
-    float kk[8], qv[8];
-    const size_t kbase = (((size_t)b * p.T + t) * p.Hk + kh) * D + 8 * m;
+    for (int c = 0; c < CT; ++c) {
+      const int j = 16 * (wave * CT + c) + l16;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { kk[e] = ld<kBf16>(p.k, kbase + e); qv[e] = ld<kBf16>(p.q, kbase + e); }
-    const size_t gi = ((size_t)b * p.T + t) * p.Hv + h;
-    const float a = p.a[gi], beta = p.beta[gi];
-    const bool round_now = ((t + 1) % p.chunk == 0) || (t == p.T - 1);
-#pragma unroll
-    for (int pass = 0; pass < PASSES; ++pass) {
-      const int j = pass * CPB + wave * CPW + lane / LPC;
-      float dk = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dk += S[pass][e] * kk[e];
-      dk = seg_sum<LPC>(dk);
-      const size_t vi = gi * D + j;
-      const float u = beta * (ld<kBf16>(p.v, vi) - a * dk);
-      float oq = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        S[pass][e] = a * S[pass][e] + kk[e] * u;
-        oq += S[pass][e] * qv[e];
+      for (int kt = 0; kt < KT; ++kt) {
+        const int m = 2 * kt + (qd >> 1);
+        const int u = (m & 3) * (D / 32) + (m >> 2);
+        c4[c][kt] = *(const uint32_t*)(rec.base + (size_t)j * (D * ub / 8) + u * ub + sel8);
+        const int e = j * rec.NG + (16 * kt) / p.group;
+        sc[c][kt] = rec.scales[e];
+        zb[c][kt] = p.asym ? zsrc[is8 ? e : (e >> 1)] : 0;
       }
-      oq = seg_sum<LPC>(oq);
-      if (m == 0) {
-        if (kBf16) ((uint16_t*)p.o)[vi] = f32_to_bf16_rne(oq);
-        else ((float*)p.o)[vi] = oq;
+    }
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int j = 16 * (wave * CT + c) + l16;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const int e = j * rec.NG + (16 * kt) / p.group;
+        const float s = bf16_to_f32(sc[c][kt]);
+        int z = 1 << (rec.bits - 1);
+        if (p.asym) z = is8 ? (int)zb[c][kt] : (int)((zb[c][kt] >> (4 * (e & 1))) & 15);
+        const uint32_t w = is8 ? c4[c][kt] : ((c4[c][kt] >> (4 * (qd & 1))) & 0x0F0F0F0Fu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[c][kt][i] = s * ((float)((w >> (8 * i)) & 0xFFu) - (float)z);
       }
-      if (round_now) requant_unit<D>(r, j, m, S[pass]);
     }
   }
+
+  const int nsb = (p.T + kSB - 1) / kSB;
+  I in;
+  load_inputs<D, IO>(in, p, b, h, kh, 0, min(kSB, p.T), tid);
+
+  for (int sb = 0; sb < nsb; ++sb) {
+    const int t0 = sb * kSB;
+    const int nt = min(kSB, p.T - t0);
+    // ---------------------------------------------------------------- inputs -> LDS
+#pragma unroll
+    for (int it = 0; it < I::NV; ++it) {
+      const int i = tid + it * kThreads;
+      const int t = i / I::VPR, c = (i % I::VPR) * VS;
+      put8<IO>(&sm.K[t][c], in.k[it]);
+      put8<IO>(&sm.Q[t][c], in.q[it]);
+      put8<IO>(&sm.U[t][c], in.v[it]);
+    }
+    if (wave == 0) {
+      // inclusive scan of log a over the 64 tokens (a = 0 is clamped to e^-80)
+      float x = fmaxf(logf(in.a), -80.f);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      sm.g[lane] = x;
+      sm.beta[lane] = in.beta;
+    }
+    // prefetch the next sub-block while this one is computed
+    if (sb + 1 < nsb) load_inputs<D, IO>(in, p, b, h, kh, t0 + kSB, min(kSB, p.T - t0 - kSB), tid);
+    __syncthreads();
+
+    // ------------------------------------------- Gram and query-key tiles (lower)
+    // jobs: 10 lower-triangular token-tile pairs for K K^T and for Q K^T
+    for (int job = wave; job < 2 * TT * (TT + 1) / 2; job += 4) {
+      const bool isq = job >= TT * (TT + 1) / 2;
+      int pr = isq ? job - TT * (TT + 1) / 2 : job;
+      int ti = 0;
+      while (pr > ti) { pr -= ti + 1; ++ti; }
+      const int tj = pr;
+      const float(*X)[Smem<D>::LD] = isq ? sm.Q : sm.K;
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < D / 16; ++v) {
+        const float4 xa = *(const float4*)&X[16 * ti + l16][16 * v + 4 * qd];
+        const float4 xb = *(const float4*)&sm.K[16 * tj + l16][16 * v + 4 * qd];
+        acc = mfma4(xa.x, xb.x, acc);
+        acc = mfma4(xa.y, xb.y, acc);
+        acc = mfma4(xa.z, xb.z, acc);
+        acc = mfma4(xa.w, xb.w, acc);
+      }
+      const int i = 16 * tj + l16;
+      const float gi = sm.g[i];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * qd + r;
+        const float dec = expf(fminf(sm.g[t] - gi, 0.f));
+        if (isq) sm.P[t][i] = t >= i ? dec * acc[r] : 0.f;
+        else sm.A[t][i] = t > i ? sm.beta[t] * dec * acc[r] : 0.f;
+      }
+    }
+
+    // ------------------------ right-hand sides diag(beta) V - diag(beta Gamma) K S
+    v4f R[CT][TT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int j = 16 * (wave * CT + c) + l16;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * tt + 4 * qd + r;
+          R[c][tt][r] = sm.beta[t] * sm.U[t][j];
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = 16 * tt + l16;
+      const float sc = -sm.beta[t] * expf(sm.g[t]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const float4 kx = *(const float4*)&sm.K[t][16 * kt + 4 * qd];
+        const float k0 = kx.x * sc, k1 = kx.y * sc, k2 = kx.z * sc, k3 = kx.w * sc;
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          R[c][tt] = mfma4(k0, S[c][kt][0], R[c][tt]);
+          R[c][tt] = mfma4(k1, S[c][kt][1], R[c][tt]);
+          R[c][tt] = mfma4(k2, S[c][kt][2], R[c][tt]);
+          R[c][tt] = mfma4(k3, S[c][kt][3], R[c][tt]);
+        }
+      }
+    }
+    __syncthreads();     // A, P complete; every wave is done reading its V columns
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int j = 16 * (wave * CT + c) + l16;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.U[16 * tt + 4 * qd + r][j] = R[c][tt][r];
+    }
+    __syncthreads();
+
+    // -------------------------------- forward solve (I + A) U = R, one column per lane
+    {
+      const int j = 16 * CT * wave + (lane % (16 * CT));
+      float u[kSB];
+#pragma unroll
+      for (int t = 0; t < kSB; ++t) u[t] = 0.f;
+#pragma unroll
+      for (int t = 0; t < kSB; ++t) {
+        float s0 = sm.U[t][j], s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+        for (int i = 0; i < t; i += 4) {
+          const float4 av = *(const float4*)&sm.A[t][i];   // entries i >= t are zero
+          s0 = fmaf(-av.x, u[i], s0);
+          s1 = fmaf(-av.y, u[i + 1], s1);
+          s2 = fmaf(-av.z, u[i + 2], s2);
+          s3 = fmaf(-av.w, u[i + 3], s3);
+        }
+        u[t] = (s0 + s1) + (s2 + s3);
+      }
+      if (lane < 16 * CT) {
+#pragma unroll
+        for (int t = 0; t < kSB; ++t) sm.U[t][j] = u[t];
+      }
+    }
+    __syncthreads();
+
+    // ----------------------------- outputs O = diag(Gamma) Q S + P U, own columns
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      v4f O[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) O[c] = v4f{0.f, 0.f, 0.f, 0.f};
+      const int tr = 16 * tt + l16;
+      const float gq = expf(sm.g[tr]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const float4 qx = *(const float4*)&sm.Q[tr][16 * kt + 4 * qd];
+        const float q0 = qx.x * gq, q1 = qx.y * gq, q2 = qx.z * gq, q3 = qx.w * gq;
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          O[c] = mfma4(q0, S[c][kt][0], O[c]);
+          O[c] = mfma4(q1, S[c][kt][1], O[c]);
+          O[c] = mfma4(q2, S[c][kt][2], O[c]);
+          O[c] = mfma4(q3, S[c][kt][3], O[c]);
+        }
+      }
+#pragma unroll
+      for (int ib = 0; ib <= tt; ++ib) {
+        const float4 px = *(const float4*)&sm.P[tr][16 * ib + 4 * qd];
+        const float pv[4] = {px.x, px.y, px.z, px.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int c = 0; c < CT; ++c)
+            O[c] = mfma4(pv[s], sm.U[16 * ib + 4 * qd + s][16 * (wave * CT + c) + l16], O[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int j = 16 * (wave * CT + c) + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * tt + 4 * qd + r;
+          if (t < nt) {
+            const size_t oi = (((size_t)b * p.T + t0 + t) * p.Hv + h) * D + j;
+            if constexpr (IO == 1) ((uint16_t*)p.o)[oi] = f32_to_bf16_rne(O[c][r]);
+            else ((float*)p.o)[oi] = O[c][r];
+          }
+        }
+      }
+    }
+
+    // --------------------------- state S' = Gamma_end S + K^T diag(e^{g_end - g}) U
+    {
+      const float gend = sm.g[kSB - 1];
+      const float ge = expf(gend);
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) S[c][kt] *= ge;
+#pragma unroll
+      for (int tb = 0; tb < TT; ++tb) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int tok = 16 * tb + 4 * qd + s;
+          const float w = expf(gend - sm.g[tok]);
+          float uv[CT];
+#pragma unroll
+          for (int c = 0; c < CT; ++c) uv[c] = sm.U[tok][16 * (wave * CT + c) + l16];
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            const float kv = sm.K[tok][16 * kt + l16] * w;
+#pragma unroll
+            for (int c = 0; c < CT; ++c) S[c][kt] = mfma4(kv, uv[c], S[c][kt]);
+          }
+        }
+      }
+    }
+
+    // ---------------------------------- rounding at chunk ends and after the last token
+    const int done = t0 + nt;
+    if (done % p.chunk == 0 || done == p.T) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int j = 16 * (wave * CT + c) + l16;
+        if (p.group == 64) requant_tile<D, 64>(S[c], rec, j, qd);
+        else requant_tile<D, 32>(S[c], rec, j, qd);
+      }
+    }
+    __syncthreads();     // the next sub-block overwrites K, Q, U, A, P
+  }
+}
+
+template <int D, int IO>
+void launch_wy(const PrefillParams& p, hipStream_t stream) {
+  const unsigned grid = (unsigned)p.B * (unsigned)p.Hv;
+  hipLaunchKernelGGL((prefill_wy_kernel<D, IO>), dim3(grid), dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace
@@ -206,13 +463,12 @@ size_t prefill_workspace_bytes(int B, int Hv, int dk, int dv, int T, int chunk) 
 
 hipError_t launch_prefill(const PrefillParams& p, int dk, int dv, int io_bf16, hipStream_t stream) {
   (void)dv;
-  const unsigned grid = (unsigned)p.B * (unsigned)p.Hv;
   if (dk == 128) {
-    if (io_bf16) hipLaunchKernelGGL((prefill_seq_kernel<128, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((prefill_seq_kernel<128, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+    if (io_bf16) launch_wy<128, 1>(p, stream);
+    else launch_wy<128, 0>(p, stream);
   } else {
-    if (io_bf16) hipLaunchKernelGGL((prefill_seq_kernel<64, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((prefill_seq_kernel<64, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+    if (io_bf16) launch_wy<64, 1>(p, stream);
+    else launch_wy<64, 0>(p, stream);
   }
   return hipGetLastError();
 }
