@@ -9,6 +9,9 @@
 // log-decays g_t (Gamma_t = e^{g_t}) and starting state S:
 //   A = strictly lower [beta_t e^{g_t - g_i} k_t . k_i]
 //   (I + A) U = diag(beta) V - diag(beta Gamma) K S                   (forward solve)
+// The solve is blocked by 16 tokens: the four 16x16 unit-lower diagonal blocks are
+// inverted by substitution, and U_i = (I + A_ii)^{-1} (R_i - sum_{j<i} A_ij U_j) runs on
+// MFMA with U kept in accumulators.
 //   O = diag(Gamma) Q S + (lower-incl [e^{g_t - g_i} q_t . k_i]) U
 //   S' = Gamma_end S + K^T diag(e^{g_end - g}) U
 // which is the token loop's result exactly in real arithmetic.  Every contraction runs on
@@ -164,8 +167,9 @@ struct Smem {
   static constexpr int LA = kSB + 4;
   float K[kSB][LD];                    // keys of the sub-block
   float Q[kSB][LD];                    // queries
-  float U[kSB][LD];                    // values, then right-hand sides, then U
+  float V[kSB][LD];                    // values
   float A[kSB][LA];                    // beta_t e^{g_t-g_i} k_t.k_i, strictly lower
+  float Ti[kSB / 16][16][20];          // inverses of the diagonal blocks (I + A_ii)
   float P[kSB][LA];                    // e^{g_t-g_i} q_t.k_i, lower incl. diagonal
   float g[kSB];                        // cumulative log decay
   float beta[kSB];
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
       const int t = i / I::VPR, c = (i % I::VPR) * VS;
       put8<IO>(&sm.K[t][c], in.k[it]);
       put8<IO>(&sm.Q[t][c], in.q[it]);
-      put8<IO>(&sm.U[t][c], in.v[it]);
+      put8<IO>(&sm.V[t][c], in.v[it]);
     }
     if (wave == 0) {
       // inclusive scan of log a over the 64 tokens (a = 0 is clamped to e^-80)
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * tt + 4 * qd + r;
-          R[c][tt][r] = sm.beta[t] * sm.U[t][j];
+          R[c][tt][r] = sm.beta[t] * sm.V[t][j];
         }
     }
 #pragma unroll
@@ -325,42 +329,51 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
         }
       }
     }
-    __syncthreads();     // A, P complete; every wave is done reading its V columns
+    __syncthreads();     // A and P complete
+
+    // ------------- inverse of diagonal block `wave`: lanes 0..15 = columns of (I + A_ww)^-1
+    {
+      const int cc = lane & 15, base = 16 * wave;
+      float x[16];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const int j = 16 * (wave * CT + c) + l16;
+      for (int t = 0; t < 16; ++t) {
+        float acc = t == cc ? 1.f : 0.f;
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+        for (int i = 0; i < t; ++i) acc = fmaf(-sm.A[base + t][base + i], x[i], acc);
+        x[t] = acc;
+      }
+      if (lane < 16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.U[16 * tt + 4 * qd + r][j] = R[c][tt][r];
+        for (int t = 0; t < 16; ++t) sm.Ti[wave][t][cc] = x[t];
+      }
     }
     __syncthreads();
 
-    // -------------------------------- forward solve (I + A) U = R, one column per lane
-    {
-      const int j = 16 * CT * wave + (lane % (16 * CT));
-      float u[kSB];
+    // --------- blocked forward solve: U_i = Ti_i (R_i - sum_{j<i} A_ij U_j), accumulators
+    v4f U[CT][TT];
 #pragma unroll
-      for (int t = 0; t < kSB; ++t) u[t] = 0.f;
+    for (int ib = 0; ib < TT; ++ib) {
+      v4f acc[CT];
 #pragma unroll
-      for (int t = 0; t < kSB; ++t) {
-        float s0 = sm.U[t][j], s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      for (int c = 0; c < CT; ++c) acc[c] = R[c][ib];
 #pragma unroll
-        for (int i = 0; i < t; i += 4) {
-          const float4 av = *(const float4*)&sm.A[t][i];   // entries i >= t are zero
-          s0 = fmaf(-av.x, u[i], s0);
-          s1 = fmaf(-av.y, u[i + 1], s1);
-          s2 = fmaf(-av.z, u[i + 2], s2);
-          s3 = fmaf(-av.w, u[i + 3], s3);
-        }
-        u[t] = (s0 + s1) + (s2 + s3);
+      for (int jb = 0; jb < ib; ++jb) {
+        const float4 av = *(const float4*)&sm.A[16 * ib + l16][16 * jb + 4 * qd];
+        const float na[4] = {-av.x, -av.y, -av.z, -av.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < CT; ++c) acc[c] = mfma4(na[r], U[c][jb][r], acc[c]);
       }
-      if (lane < 16 * CT) {
+      const float4 tv = *(const float4*)&sm.Ti[ib][l16][4 * qd];
+      const float ti[4] = {tv.x, tv.y, tv.z, tv.w};
 #pragma unroll
-        for (int t = 0; t < kSB; ++t) sm.U[t][j] = u[t];
+      for (int c = 0; c < CT; ++c) {
+        U[c][ib] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) U[c][ib] = mfma4(ti[r], acc[c][r], U[c][ib]);
       }
     }
-    __syncthreads();
 
     // ----------------------------- outputs O = diag(Gamma) Q S + P U, own columns
 #pragma unroll
@@ -390,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
         for (int s = 0; s < 4; ++s)
 #pragma unroll
           for (int c = 0; c < CT; ++c)
-            O[c] = mfma4(pv[s], sm.U[16 * ib + 4 * qd + s][16 * (wave * CT + c) + l16], O[c]);
+            O[c] = mfma4(pv[s], U[c][ib][s], O[c]);
       }
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
@@ -421,14 +434,11 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
         for (int s = 0; s < 4; ++s) {
           const int tok = 16 * tb + 4 * qd + s;
           const float w = expf(gend - sm.g[tok]);
-          float uv[CT];
-#pragma unroll
-          for (int c = 0; c < CT; ++c) uv[c] = sm.U[tok][16 * (wave * CT + c) + l16];
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
             const float kv = sm.K[tok][16 * kt + l16] * w;
 #pragma unroll
-            for (int c = 0; c < CT; ++c) S[c][kt] = mfma4(kv, uv[c], S[c][kt]);
+            for (int c = 0; c < CT; ++c) S[c][kt] = mfma4(kv, U[c][tb][s], S[c][kt]);
           }
         }
       }
@@ -444,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
         else requant_tile<D, 32>(S[c], rec, j, qd);
       }
     }
-    __syncthreads();     // the next sub-block overwrites K, Q, U, A, P
+    __syncthreads();     // the next sub-block overwrites K, Q, V, A, P
   }
 }
 
