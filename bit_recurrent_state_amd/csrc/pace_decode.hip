@@ -83,8 +83,8 @@ struct alignas(16) Smem {
   } pw;
   alignas(16) uint16_t kT[CH][D][8];        // key codes as bf16, rows in (tile, row) order
   alignas(16) float G[NV][NV];              // Gram matrix of the slots (scaled)
-  alignas(16) uint16_t scales[D * 4];       // this tile's scales, [col][group]
-  alignas(16) uint8_t zeros[D * 4];         // this tile's zero points (raw bytes)
+  alignas(16) float scf[D * 4];             // this tile's scales as fp32, [col][group]
+  alignas(16) uint8_t zeros[D * 4];         // this tile's zero points, one byte each
   float vscale[NV];                         // key scale of each token slot / q piece scale
   float vs[TOK], ga[TOK], gb[TOK];
   float red[3][kWaves];
@@ -96,7 +96,10 @@ struct alignas(16) Smem {
 // GT: scale-group size (32 or 64), 0 = taken from the parameters at run time.
 // AS: 0 = symmetric, 1 = asymmetric, 2 = taken from the parameters at run time.
 template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+// Eight resident workgroups per CU (four waves per SIMD) for the dP <= 8 variants, so a
+// 2048-tile launch runs in one round: at most 128 VGPRs.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOK <= 8 ? 4 : 1)))
+void decode_kernel(DecodeParams p) {
   using SM = Smem<D, TOK>;
   constexpr int NV = SM::NV;
   constexpr int NT = NV / 16;           // 16-vector MFMA column tiles
@@ -118,6 +121,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // issue all of them before the first wait.
   int32_t* countp = (int32_t*)p.buffer + (size_t)b * p.Hv + h;
   const int count_raw = *countp;
+  __builtin_amdgcn_sched_barrier(0);          // issue the count load first
 
   const bool is8 = HB == 8 ? true : (HB == 4 ? false : ((p.mask8 >> h) & 1ull) != 0);
   const int bits = is8 ? 8 : 4;
@@ -136,7 +140,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // The loads are issued in the order they are consumed (the memory counters complete
   // in order): the active flag and the current token first, so that the token can be
   // quantised while the state codes and the buffered tokens are still in flight.
-  if (flush_only && count_raw <= 0) return;   // nothing buffered: nothing to flush
   // branch-free: without a mask the load reads an in-bounds stand-in and is ignored
   const uint8_t mask_v = *(p.mask ? p.mask + b : (const uint8_t*)countp);
   const bool active = !p.mask || mask_v != 0;
@@ -181,6 +184,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const uint4 sc_reg = ((const uint4*)g_scales)[min(tid, sc_vec - 1)];
   const uint4 zp_reg = ((const uint4*)(asym ? (const uint8_t*)g_zeros : (const uint8_t*)g_scales))[min(tid, zp_vec - 1)];
 
+  // the state stream is in flight before the first use of the count
+  __builtin_amdgcn_sched_barrier(0);
+
   // counts outside [0, dP) cannot come from this library; clamp so that every slot
   // index stays inside the buffer whatever the buffer holds
   const int n0 = min(max(count_raw, 0), p.dP - 1);
@@ -224,10 +230,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const float a_t = __shfl(a_row, h);
   const float b_t = __shfl(b_row, h);
   __syncthreads();
-  // Inactive tiles leave here, after the barrier: an exit before it would let the
-  // compiler hold every load back until the flag has arrived.  The flag is uniform
-  // over the workgroup, so the whole tile leaves together.
-  if (!active) return;
+  // Inactive tiles (and flushes of an empty buffer) leave here, after the barrier: an
+  // exit before it would hold every load back until the flag and the count have arrived.
+  // Both are uniform over the workgroup, so the whole tile leaves together.
+  if (!active || (flush_only && count_raw <= 0)) return;   // (nothing buffered: nothing to flush)
   if (!flush_only) {
     float Mk = sm.red[0][0], Mv = sm.red[1][0], Mq = sm.red[2][0];
 #pragma unroll
@@ -345,8 +351,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       *(uint4*)&sm.kc[row][16 * (i % RV)] = make_uint4(0, 0, 0, 0);
   }
   if (tid >= n && tid < NV && (tid < QS || flush_only || tid >= QS + 3)) sm.vscale[tid] = 0.f;
-  if (tid < sc_vec) ((uint4*)sm.scales)[tid] = sc_reg;
-  if (asym && tid < zp_vec) ((uint4*)sm.zeros)[tid] = zp_reg;
+  if (tid < sc_vec) {                       // 8 bf16 scales -> fp32
+    const uint32_t w[4] = {sc_reg.x, sc_reg.y, sc_reg.z, sc_reg.w};
+    float4* dst = (float4*)&sm.scf[8 * tid];
+    dst[0] = make_float4(bits_f32(w[0] << 16), bits_f32(w[0] & 0xFFFF0000u), bits_f32(w[1] << 16), bits_f32(w[1] & 0xFFFF0000u));
+    dst[1] = make_float4(bits_f32(w[2] << 16), bits_f32(w[2] & 0xFFFF0000u), bits_f32(w[3] << 16), bits_f32(w[3] & 0xFFFF0000u));
+  }
+  if (asym && tid < zp_vec) {
+    if (is8) {
+      ((uint4*)sm.zeros)[tid] = zp_reg;
+    } else {                                 // 32 packed 4-bit zero points -> one byte each
+      const uint32_t w[4] = {zp_reg.x, zp_reg.y, zp_reg.z, zp_reg.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // bytes b0..b3 hold zero points (2i, 2i+1) in (low, high) nibbles
+        const uint32_t lo = w[e] & 0x0F0F0F0Fu, hi = (w[e] >> 4) & 0x0F0F0F0Fu;
+        o[2 * e] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);       // lo0 hi0 lo1 hi1
+        o[2 * e + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // lo2 hi2 lo3 hi3
+      }
+      uint4* dst = (uint4*)&sm.zeros[32 * tid];
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  }
   __syncthreads();
   if (BUF == PACE_BUF_K4_VBF16 && !flush_only && !do_flush && (h % p.gamma) == 0 && tid < D / 2) {
     const int m = tid / 4, w = tid % 4;
@@ -424,14 +452,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = ocol + i;
-        const float sc = bf16_to_f32(sm.scales[c * NG + g]);
-        int z;
-        if (asym) {
-          const int e = c * NG + g;
-          z = is8 ? (int)sm.zeros[e] : (int)((sm.zeros[e >> 1] >> (4 * (e & 1))) & 15);
-        } else {
-          z = 1 << (bits - 1);
-        }
+        const float sc = sm.scf[c * NG + g];
+        int z = asym ? (int)sm.zeros[c * NG + g] : 1 << (bits - 1);
         if (is8) z -= 128;                // the A operand held codes - 128
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -543,19 +565,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int g = kb / kpg;
-      const float sc = bf16_to_f32(sm.scales[c * NG + g]);
-      int z;
-      if (asym) {
-        const int e = c * NG + g;
-        z = is8 ? (int)sm.zeros[e] : (int)((sm.zeros[e >> 1] >> (4 * (e & 1))) & 15);
-      } else {
-        z = 1 << (bits - 1);
-      }
+      const float sc = sm.scf[c * NG + g];
+      const int z = asym ? (int)sm.zeros[c * NG + g] : 1 << (bits - 1);
       const float gs = gn * sc, gz = -gs * (float)z;
       uint32_t b0, b1;            // 4 stored codes each (bytes): keys +0..3, +4..7
       if (!is8) {
         b0 = araw[s][kb] & 0x0F0F0F0Fu;
         b1 = (araw[s][kb] >> 4) & 0x0F0F0F0Fu;
+        // keep the masks whole-word, so that each byte converts in one instruction
+        asm("" : "+v"(b0));
+        asm("" : "+v"(b1));
       } else if constexpr (HB != 4) {
         b0 = araw[s][2 * kb];
         b1 = araw[s][2 * kb + 1];
@@ -591,28 +610,43 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     for (int g = 0; g < 4; ++g) {
       if (g >= NG) break;
       float mx = -INFINITY, mn = INFINITY;
+      if (asym) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        if (kb / kpg != g) continue;
+        for (int kb = 0; kb < KB; ++kb) {
+          if (kb / kpg != g) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          mx = fmaxf(mx, fmaxf(acc[2 * kb][i], acc[2 * kb + 1][i]));
-          mn = fminf(mn, fminf(acc[2 * kb][i], acc[2 * kb + 1][i]));
+          for (int i = 0; i < 4; ++i) {
+            mx = fmaxf(mx, fmaxf(acc[2 * kb][i], acc[2 * kb + 1][i]));
+            mn = fminf(mn, fminf(acc[2 * kb][i], acc[2 * kb + 1][i]));
+          }
         }
+        mx = fmaxf(mx, __shfl_xor(mx, 16)); mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mn = fminf(mn, __shfl_xor(mn, 16)); mn = fminf(mn, __shfl_xor(mn, 32));
+      } else {                    // symmetric: only max |x| matters
+        mx = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          if (kb / kpg != g) continue;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(fabsf(acc[2 * kb][i]), fabsf(acc[2 * kb + 1][i])));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16)); mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mn = -mx;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16)); mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mn = fminf(mn, __shfl_xor(mn, 16)); mn = fminf(mn, __shfl_xor(mn, 32));
       const GroupQuant gq = group_quant(mn, mx, asym, bits);
       const CodeRange cr = code_range(gq.z, asym, bits);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         if (kb / kpg != g) continue;
-        uint32_t lo = 0, hi = 0;
+        // codes as the low bytes of clamped fma results; gathered four at a time
+        uint32_t f0[4], f1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          lo |= (uint32_t)code_of(acc[2 * kb][i], gq.r, cr.magic, cr.lo, cr.hi) << (8 * i);
-          hi |= (uint32_t)code_of(acc[2 * kb + 1][i], gq.r, cr.magic, cr.lo, cr.hi) << (8 * i);
+          f0[i] = f32_bits(fminf(fmaxf(fmaf(acc[2 * kb][i], gq.r, cr.magic), cr.lo), cr.hi));
+          f1[i] = f32_bits(fminf(fmaxf(fmaf(acc[2 * kb + 1][i], gq.r, cr.magic), cr.lo), cr.hi));
         }
+        const uint32_t lo = __builtin_amdgcn_perm(f0[1], f0[0], 0x0c0c0400u) | __builtin_amdgcn_perm(f0[3], f0[2], 0x04000c0cu);
+        const uint32_t hi = __builtin_amdgcn_perm(f1[1], f1[0], 0x0c0c0400u) | __builtin_amdgcn_perm(f1[3], f1[2], 0x04000c0cu);
         if (!is8) {
           outw[kb] = lo | (hi << 4);
         } else if constexpr (HB != 4) {
