@@ -50,10 +50,25 @@ __device__ inline void store_io(void* p, size_t i, float x) {
   else ((float*)p)[i] = x;
 }
 
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+// Lane permutations inside rows of 16 lanes (DPP): quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror, row_mirror.
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over each row of 16 lanes; every lane of the row ends with it.
+__device__ inline float row_max16(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
   return x;
+}
+
+// x of lane (addr / 4), addr precomputed once per thread.
+__device__ inline float lane_read(int addr, float x) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
 }
 
 // Sum of the 8 signed bytes of v.
@@ -87,7 +102,7 @@ struct alignas(16) Smem {
   alignas(16) uint8_t zeros[D * 4];         // this tile's zero points, one byte each
   float vscale[NV];                         // key scale of each token slot / q piece scale
   float vs[TOK], ga[TOK], gb[TOK];
-  float red[3][kWaves];
+  float red[3][4 * kWaves];                 // row maxima of |k|, |v|, |q|
   float gamma_n;
 };
 
@@ -222,13 +237,13 @@ void decode_kernel(DecodeParams p) {
 
   // ---------------------------------- current token -> buffer (loads still in flight)
   {
-    const float m0 = wave_max(tid < D ? fabsf(kx) : 0.f);
-    const float m1 = wave_max(tid < D ? fabsf(vx) : 0.f);
-    const float m2 = wave_max(tid < D ? fabsf(qx) : 0.f);
-    if (lane == 0) { sm.red[0][wave] = m0; sm.red[1][wave] = m1; sm.red[2][wave] = m2; }
+    const float m0 = row_max16(tid < D ? fabsf(kx) : 0.f);
+    const float m1 = row_max16(tid < D ? fabsf(vx) : 0.f);
+    const float m2 = row_max16(tid < D ? fabsf(qx) : 0.f);
+    if (l16 == 0) { sm.red[0][4 * wave + qq] = m0; sm.red[1][4 * wave + qq] = m1; sm.red[2][4 * wave + qq] = m2; }
   }
-  const float a_t = __shfl(a_row, h);
-  const float b_t = __shfl(b_row, h);
+  const float a_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a_row), h));
+  const float b_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b_row), h));
   __syncthreads();
   // Inactive tiles (and flushes of an empty buffer) leave here, after the barrier: an
   // exit before it would hold every load back until the flag and the count have arrived.
@@ -237,7 +252,7 @@ void decode_kernel(DecodeParams p) {
   if (!flush_only) {
     float Mk = sm.red[0][0], Mv = sm.red[1][0], Mq = sm.red[2][0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
+    for (int w = 1; w < 4 * kWaves; ++w) {
       Mk = fmaxf(Mk, sm.red[0][w]); Mv = fmaxf(Mv, sm.red[1][w]); Mq = fmaxf(Mq, sm.red[2][w]);
     }
     const float kq_max = BUF == PACE_BUF_INT8 ? 127.f : 7.f;
@@ -383,24 +398,21 @@ void decode_kernel(DecodeParams p) {
   }
 
   // --------------------------------------------- B operands, group sums, Gram
+  // per-group code sums of every slot vector, from an MFMA against all-ones rows (the
+  // zero-point term of the projections); every output row holds the same sums
   long bop[NT][KB];
   int ksum[NT][4];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) ksum[nt][g] = 0;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bop[nt][kb] = *(const long*)&sm.kc[nt * 16 + l16][32 * kb + 8 * qq];
-      const int s = sum8(bop[nt][kb]);
-      const int g = kb / kpg;
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) ksum[nt][gg] += (gg == g) ? s : 0;
-    }
+    for (int kb = 0; kb < KB; ++kb) bop[nt][kb] = *(const long*)&sm.kc[nt * 16 + l16][32 * kb + 8 * qq];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      ksum[nt][g] += __shfl_xor(ksum[nt][g], 16);
-      ksum[nt][g] += __shfl_xor(ksum[nt][g], 32);
+      v4i ks = {0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        if (kb / kpg == g) ks = __builtin_amdgcn_mfma_i32_16x16x32_i8(0x0101010101010101l, bop[nt][kb], ks, 0, 0, 0);
+      ksum[nt][g] = ks[0];
     }
   }
   if (wave == kWaves - 1) {
@@ -557,6 +569,7 @@ void decode_kernel(DecodeParams p) {
 
   // ----------------------------------------- flush: fold on MFMA, requantise
   const float gn = sm.gamma_n;
+  const int ax16 = (lane ^ 16) << 2, ax32 = (lane ^ 32) << 2;   // lanes of the other quarters
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     const int c = (wave + kWaves * s) * 16 + l16;    // this lane's column
@@ -620,8 +633,8 @@ void decode_kernel(DecodeParams p) {
             mn = fminf(mn, fminf(acc[2 * kb][i], acc[2 * kb + 1][i]));
           }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16)); mx = fmaxf(mx, __shfl_xor(mx, 32));
-        mn = fminf(mn, __shfl_xor(mn, 16)); mn = fminf(mn, __shfl_xor(mn, 32));
+        mx = fmaxf(mx, lane_read(ax16, mx)); mx = fmaxf(mx, lane_read(ax32, mx));
+        mn = fminf(mn, lane_read(ax16, mn)); mn = fminf(mn, lane_read(ax32, mn));
       } else {                    // symmetric: only max |x| matters
         mx = 0.f;
 #pragma unroll
@@ -630,7 +643,7 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(fabsf(acc[2 * kb][i]), fabsf(acc[2 * kb + 1][i])));
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16)); mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, lane_read(ax16, mx)); mx = fmaxf(mx, lane_read(ax32, mx));
         mn = -mx;
       }
       const GroupQuant gq = group_quant(mn, mx, asym, bits);
