@@ -98,6 +98,7 @@ struct alignas(16) Smem {
   } pw;
   alignas(16) uint16_t kT[CH][D][8];        // key codes as bf16, rows in (tile, row) order
   alignas(16) float G[NV][NV];              // Gram matrix of the slots (scaled)
+  float Gq[NV];                             // k_slot . q (the q pieces combined)
   alignas(16) float scf[D * 4];             // this tile's scales as fp32, [col][group]
   alignas(16) uint8_t zeros[D * 4];         // this tile's zero points, one byte each
   float vscale[NV];                         // key scale of each token slot / q piece scale
@@ -256,14 +257,15 @@ void decode_kernel(DecodeParams p) {
       Mk = fmaxf(Mk, sm.red[0][w]); Mv = fmaxf(Mv, sm.red[1][w]); Mq = fmaxf(Mq, sm.red[2][w]);
     }
     const float kq_max = BUF == PACE_BUF_INT8 ? 127.f : 7.f;
-    const float ks = Mk / kq_max;       // IEEE division: the fp32 buffer scale
+    // the fp32 buffer scales M / 127 (M / 7), correctly rounded
+    const float ks = div_rn(Mk, kq_max, BUF == PACE_BUF_INT8 ? 1.0f / 127.0f : 1.0f / 7.0f);
     if (tid < D) {
       const float kcf = ks > 0.f ? fminf(fmaxf(rintf(kx / ks), -kq_max), kq_max) : 0.f;
       sm.kc[n0][tid] = (int8_t)kcf;
       int8_t vcode = 0;
       float vs = 0.f;
       if (BUF == PACE_BUF_INT8) {
-        vs = Mv / 127.f;
+        vs = div_rn(Mv, 127.f, 1.0f / 127.0f);
         vcode = (int8_t)(vs > 0.f ? fminf(fmaxf(rintf(vx / vs), -127.f), 127.f) : 0.f);
         sm.v.c[n0][tid] = vcode;
       } else {
@@ -398,21 +400,25 @@ void decode_kernel(DecodeParams p) {
   }
 
   // --------------------------------------------- B operands, group sums, Gram
-  // per-group code sums of every slot vector, from an MFMA against all-ones rows (the
-  // zero-point term of the projections); every output row holds the same sums
+  // Zero-point term of the projections, per scale group and slot vector, on MFMA with a
+  // constant A operand (every output row holds the same value): symmetric 4-bit states
+  // store c + 8, so each group's projection carries -8 * (sum of the slot's codes over the
+  // group) and an A of -8 bytes produces exactly that term, which then seeds the group's
+  // accumulator; symmetric 8-bit codes enter the MFMA as c itself (no term); asymmetric
+  // zero points vary by column, so there the plain sums are formed (A of ones).
   long bop[NT][KB];
-  int ksum[NT][4];
+  v4i zacc[NT][4];
+  const long zrow = asym ? 0x0101010101010101l : (is8 ? 0l : (long)0xF8F8F8F8F8F8F8F8ull);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) bop[nt][kb] = *(const long*)&sm.kc[nt * 16 + l16][32 * kb + 8 * qq];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      v4i ks = {0, 0, 0, 0};
+      zacc[nt][g] = v4i{0, 0, 0, 0};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        if (kb / kpg == g) ks = __builtin_amdgcn_mfma_i32_16x16x32_i8(0x0101010101010101l, bop[nt][kb], ks, 0, 0, 0);
-      ksum[nt][g] = ks[0];
+        if (kb / kpg == g) zacc[nt][g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(zrow, bop[nt][kb], zacc[nt][g], 0, 0, 0);
     }
   }
   if (wave == kWaves - 1) {
@@ -428,7 +434,13 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = mt * 16 + 4 * qq + i;
-          sm.G[row][col] = (float)acc[i] * sm.vscale[row] * sm.vscale[col];
+          const float gv = (float)acc[i] * sm.vscale[row] * sm.vscale[col];
+          sm.G[row][col] = gv;
+          // k_row . q: the three q pieces sit in columns QS..QS+2 of one 16-lane row
+          if (nt == QS / 16) {
+            const float gsum = gv + dpp<0x101>(gv) + dpp<0x102>(gv);
+            if (col == QS) sm.Gq[row] = gsum;
+          }
         }
       }
     }
@@ -446,7 +458,7 @@ void decode_kernel(DecodeParams p) {
       for (int i = 0; i < 4; ++i) proj[nt][i] = 0.f;
     v4i acc[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = v4i{0, 0, 0, 0};
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = asym ? v4i{0, 0, 0, 0} : zacc[nt][0];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       long a;
@@ -459,24 +471,26 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bop[nt][kb], acc[nt], 0, 0, 0);
       if ((kb + 1) % kpg != 0) continue;
-      // end of scale group g: scale and zero point once per (column, group)
+      // end of scale group g: scale (and an asymmetric zero point) once per (column, group)
       const int g = kb / kpg;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = ocol + i;
         const float sc = sm.scf[c * NG + g];
-        int z = asym ? (int)sm.zeros[c * NG + g] : 1 << (bits - 1);
-        if (is8) z -= 128;                // the A operand held codes - 128
+        if (asym) {
+          int z = (int)sm.zeros[c * NG + g];
+          if (is8) z -= 128;              // the A operand held codes - 128
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          int ksg = 0;
+          for (int nt = 0; nt < NT; ++nt) proj[nt][i] += (float)(acc[nt][i] - z * zacc[nt][g][0]) * sc;
+        } else {
 #pragma unroll
-          for (int gg = 0; gg < 4; ++gg) ksg += (gg == g) ? ksum[nt][gg] : 0;
-          proj[nt][i] += (float)(acc[nt][i] - z * ksg) * sc;
+          for (int nt = 0; nt < NT; ++nt) proj[nt][i] += (float)acc[nt][i] * sc;
         }
       }
+      if (g + 1 < NG) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = v4i{0, 0, 0, 0};
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = asym ? v4i{0, 0, 0, 0} : zacc[nt][(g + 1) & 3];
+      }
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -493,21 +507,20 @@ void decode_kernel(DecodeParams p) {
     const int j = tid;
     float y[TOK];
 #pragma unroll
-    for (int m = 0; m < TOK; ++m) { y[m] = (m < n) ? sm.pw.P[m][j] : 0.f; u[m] = 0.f; }
+    // slots n.. hold zero codes, so their projections and Gram entries are zero and the
+    // updates below may run over them unconditionally
+    for (int m = 0; m < TOK; ++m) { y[m] = sm.pw.P[m][j]; u[m] = 0.f; }
     float yq = sm.pw.P[QS][j] + sm.pw.P[QS + 1][j] + sm.pw.P[QS + 2][j];
 #pragma unroll
     for (int i = 0; i < TOK; ++i) {
-      if (i < n) {
-        const float ai = sm.ga[i];
-        const float vh = BUF == PACE_BUF_INT8 ? (float)sm.v.c[i][j] * sm.vs[i] : bf16_to_f32(sm.v.b[i][j]);
-        const float ui = sm.gb[i] * (vh - ai * y[i]);
-        u[i] = ui;
+      if (i >= n) break;
+      const float ai = sm.ga[i];
+      const float vh = BUF == PACE_BUF_INT8 ? (float)sm.v.c[i][j] * sm.vs[i] : bf16_to_f32(sm.v.b[i][j]);
+      const float ui = sm.gb[i] * (vh - ai * y[i]);
+      u[i] = ui;
 #pragma unroll
-        for (int m = i + 1; m < TOK; ++m)
-          if (m < n) y[m] = ai * y[m] + sm.G[i][m] * ui;
-        const float gq = sm.G[i][QS] + sm.G[i][QS + 1] + sm.G[i][QS + 2];
-        yq = ai * yq + gq * ui;
-      }
+      for (int m = i + 1; m < TOK; ++m) y[m] = ai * y[m] + sm.G[i][m] * ui;
+      yq = ai * yq + sm.Gq[i] * ui;
     }
     if (!flush_only) store_io<kBf16>(p.o, ((size_t)b * p.Hv + h) * D + j, yq);
   }

@@ -56,14 +56,25 @@ __host__ __device__ inline float bf16_ceil_from_f64(double d) {
   return bits_f32(u);
 }
 
-// Smallest bf16 value >= m / k for fp32 m >= 0 and a small positive integer k, without
-// leaving fp32: q = fl(m / k) is correctly rounded; if q * k < m (decided exactly by one
-// fused multiply-add, whose product q * k needs at most 24 + 8 bits) the quotient was
-// rounded down and q is moved one fp32 ulp up; the result is then rounded up to bf16.
-// Exact because bf16 values are fp32 values.
-__host__ __device__ inline float bf16_ceil_div(float m, float k) {
+// Correctly rounded m / k from the correctly rounded reciprocal rk = fl(1 / k), in three
+// operations (Markstein's correction: q = fl(m rk) is within an ulp of m / k, the
+// residual m - q k is exact in one fused multiply-add, and fl(q + residual * rk) is the
+// correctly rounded quotient).  Used with the integer divisors 7, 15, 127 and 255, for
+// which it agrees with IEEE division on every positive fp32 m.
+__host__ __device__ inline float div_rn(float m, float k, float rk) {
+  const float q = m * rk;
+  const float e = fmaf(-q, k, m);
+  return fmaf(e, rk, q);
+}
+
+// Smallest bf16 value >= m / k for fp32 m >= 0 and a divisor k in {7, 15, 127, 255}
+// (rk = fl(1 / k)), without leaving fp32: q = fl(m / k) is correctly rounded; if q * k < m
+// (decided exactly by one fused multiply-add, whose product q * k needs at most 24 + 8
+// bits) the quotient was rounded down and q is moved one fp32 ulp up; the result is then
+// rounded up to bf16.  Exact because bf16 values are fp32 values.
+__host__ __device__ inline float bf16_ceil_div(float m, float k, float rk) {
   if (!(m > 0.0f)) return 0.0f;
-  float q = m / k;
+  float q = div_rn(m, k, rk);
   if (fmaf(q, k, -m) < 0.0f) q = bits_f32(f32_bits(q) + 1u);
   uint32_t u = f32_bits(q);
   if (u & 0xFFFFu) u = (u + 0x10000u) & 0xFFFF0000u;
@@ -107,7 +118,7 @@ __host__ __device__ inline GroupQuant group_quant(float mn, float mx, bool asym,
   const int levels = (1 << bits) - 1, zsym = 1 << (bits - 1);
   if (!asym) {
     const float M = fmaxf(fabsf(mx), fabsf(mn));
-    q.s = bf16_ceil_div(M, (float)(zsym - 1));
+    q.s = bf16_ceil_div(M, (float)(zsym - 1), bits == 8 ? 1.0f / 127.0f : 1.0f / 7.0f);
     q.z = zsym;
   } else {
     const float lo = fminf(mn, 0.f), hi = fmaxf(mx, 0.f);
@@ -115,7 +126,7 @@ __host__ __device__ inline GroupQuant group_quant(float mn, float mx, bool asym,
     // the exact range lies above its fp32 rounding
     float range = hi - lo;
     if ((double)range < (double)hi - (double)lo) range = bits_f32(f32_bits(range) + 1u);
-    q.s = bf16_ceil_div(range, (float)levels);
+    q.s = bf16_ceil_div(range, (float)levels, bits == 8 ? 1.0f / 255.0f : 1.0f / 15.0f);
     q.z = q.s > 0.f ? (int)fminf(fmaxf(rne_quotient(-lo, q.s, 1.0f / q.s), 0.f), (float)levels) : 0;
   }
   q.r = q.s > 0.f ? 1.0f / q.s : 0.f;

@@ -54,8 +54,20 @@ int main() {
     const float k = ks[i & 3];
     float m = (float)std::exp(U(rng) * 30.0);
     if (i % 5 == 0) m = ref_bf16_ceil(std::exp(U(rng) * 20.0)) * k;   // exact multiples
-    const float got = bf16_ceil_div(m, k), want = ref_bf16_ceil((double)m / (double)k);
+    const float got = bf16_ceil_div(m, k, 1.0f / k), want = ref_bf16_ceil((double)m / (double)k);
     EXPECT(got == want, "bf16_ceil_div(%.9g, %g) = %.9g want %.9g", m, k, got, want);
+    n++;
+  }
+  // correctly rounded quotient from a correctly rounded reciprocal, against IEEE division
+  for (int i = 0; i < 400000; ++i) {
+    const float ks[4] = {7.f, 15.f, 127.f, 255.f};
+    const float k = ks[i & 3];
+    uint32_t u = (uint32_t)(rng() % 0x7F000000u) + 1u;     // positive finite fp32 patterns
+    float m;
+    memcpy(&m, &u, 4);
+    volatile float km = k;
+    const float got = div_rn(m, k, 1.0f / km), want = m / km;
+    EXPECT(got == want, "div_rn(%a, %g) = %a want %a", m, k, got, want);
     n++;
   }
   // exact RNE quotient, including constructed exact ties and near ties
