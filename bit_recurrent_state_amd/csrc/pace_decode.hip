@@ -44,9 +44,21 @@ __device__ inline float load_io(const void* p, size_t i) {
   if constexpr (BF16) return bf16_to_f32(((const uint16_t*)p)[i]);
   else return ((const float*)p)[i];
 }
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest-even bf16 by the hardware conversion, packed
+// (a in the low half).
+__device__ inline uint32_t pk_bf16(float a, float b) {
+  const v2bf h = __builtin_convertvector(v2f{a, b}, v2bf);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
+}
+
 template <bool BF16>
 __device__ inline void store_io(void* p, size_t i, float x) {
-  if constexpr (BF16) ((uint16_t*)p)[i] = f32_to_bf16_rne(x);
+  if constexpr (BF16) ((uint16_t*)p)[i] = (uint16_t)pk_bf16(x, 0.f);
   else ((float*)p)[i] = x;
 }
 
@@ -269,7 +281,7 @@ void decode_kernel(DecodeParams p) {
         vcode = (int8_t)(vs > 0.f ? fminf(fmaxf(rintf(vx / vs), -127.f), 127.f) : 0.f);
         sm.v.c[n0][tid] = vcode;
       } else {
-        sm.v.b[n0][tid] = f32_to_bf16_rne(vx);
+        sm.v.b[n0][tid] = (uint16_t)pk_bf16(vx, 0.f);
       }
       // q as three exact int8 pieces with power-of-two scales s1, s1/128, s1/16384,
       // s1 = 2^(e-6) for max|q| = m 2^e (0.5 <= m < 1), so |q / s1| < 64
@@ -305,7 +317,7 @@ void decode_kernel(DecodeParams p) {
           ((int8_t*)(p.buffer + p.off_v))[(vslot0 + n0) * D + tid] = vcode;
           if (tid == 0) ((float*)(p.buffer + p.off_vs))[vslot0 + n0] = vs;
         } else {
-          ((uint16_t*)(p.buffer + p.off_v))[(vslot0 + n0) * D + tid] = f32_to_bf16_rne(vx);
+          ((uint16_t*)(p.buffer + p.off_v))[(vslot0 + n0) * D + tid] = (uint16_t)pk_bf16(vx, 0.f);
         }
         if (tid == 0) {
           if (key_writer) ks_buf[kslot0 + n0] = ks;
@@ -536,24 +548,25 @@ void decode_kernel(DecodeParams p) {
   if (tid < D) {
     const int j = tid;
     float w = 1.f;
-    uint32_t pk[3][TOK / 2];              // pieces, two bf16 per dword, token order
-#pragma unroll
-    for (int i = 0; i < TOK / 2; ++i) pk[0][i] = pk[1][i] = pk[2][i] = 0u;
+    float wv[TOK];
 #pragma unroll
     for (int i = TOK - 1; i >= 0; --i) {
-      float wi = 0.f;
+      wv[i] = 0.f;
       if (i < n) {
-        wi = w * sm.vscale[i] * u[i];
+        wv[i] = w * sm.vscale[i] * u[i];
         w *= sm.ga[i];
       }
-      const uint16_t h0 = f32_to_bf16_rne(wi);
-      const float r0 = wi - bf16_to_f32(h0);
-      const uint16_t h1 = f32_to_bf16_rne(r0);
-      const uint16_t h2 = f32_to_bf16_rne(r0 - bf16_to_f32(h1));
-      const int sh = 16 * (i & 1);
-      pk[0][i / 2] |= (uint32_t)h0 << sh;
-      pk[1][i / 2] |= (uint32_t)h1 << sh;
-      pk[2][i / 2] |= (uint32_t)h2 << sh;
+    }
+    uint32_t pk[3][TOK / 2];              // pieces, two bf16 per dword, token order
+#pragma unroll
+    for (int e = 0; e < TOK / 2; ++e) {
+      float x0 = wv[2 * e], x1 = wv[2 * e + 1];
+#pragma unroll
+      for (int pc = 0; pc < 3; ++pc) {
+        pk[pc][e] = pk_bf16(x0, x1);
+        x0 -= bits_f32(pk[pc][e] << 16);
+        x1 -= bits_f32(pk[pc][e] & 0xFFFF0000u);
+      }
     }
 #pragma unroll
     for (int ch = 0; ch < CH; ++ch) {
@@ -570,10 +583,9 @@ void decode_kernel(DecodeParams p) {
       uint32_t kw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i0 = 8 * ch + 2 * e, i1 = i0 + 1;
-        const int8_t c0 = i0 < n ? sm.kc[i0][j] : (int8_t)0;
-        const int8_t c1 = i1 < n ? sm.kc[i1][j] : (int8_t)0;
-        kw[e] = (f32_bits((float)c0) >> 16) | (f32_bits((float)c1) & 0xFFFF0000u);   // exact in bf16
+        // slots n.. hold zero codes; small integers are exact in bf16
+        const int i0 = 8 * ch + 2 * e;
+        kw[e] = pk_bf16((float)sm.kc[i0][j], (float)sm.kc[i0 + 1][j]);
       }
       *(uint4*)&sm.kT[ch][t * 16 + m][0] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
     }
@@ -665,11 +677,18 @@ void decode_kernel(DecodeParams p) {
       for (int kb = 0; kb < KB; ++kb) {
         if (kb / kpg != g) continue;
         // codes as the low bytes of clamped fma results; gathered four at a time
+        // (symmetric: |x| r <= 2^(b-1) - 1 up to one rounding, since the scale is the
+        // rounded-up max / (2^(b-1) - 1), so no clamp is needed)
         uint32_t f0[4], f1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f0[i] = f32_bits(fminf(fmaxf(fmaf(acc[2 * kb][i], gq.r, cr.magic), cr.lo), cr.hi));
-          f1[i] = f32_bits(fminf(fmaxf(fmaf(acc[2 * kb + 1][i], gq.r, cr.magic), cr.lo), cr.hi));
+          float y0 = fmaf(acc[2 * kb][i], gq.r, cr.magic), y1 = fmaf(acc[2 * kb + 1][i], gq.r, cr.magic);
+          if (asym) {
+            y0 = fminf(fmaxf(y0, cr.lo), cr.hi);
+            y1 = fminf(fmaxf(y1, cr.lo), cr.hi);
+          }
+          f0[i] = f32_bits(y0);
+          f1[i] = f32_bits(y1);
         }
         const uint32_t lo = __builtin_amdgcn_perm(f0[1], f0[0], 0x0c0c0400u) | __builtin_amdgcn_perm(f0[3], f0[2], 0x04000c0cu);
         const uint32_t hi = __builtin_amdgcn_perm(f1[1], f1[0], 0x0c0c0400u) | __builtin_amdgcn_perm(f1[3], f1[2], 0x04000c0cu);

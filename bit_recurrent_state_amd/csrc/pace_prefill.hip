@@ -93,7 +93,9 @@ __device__ inline void requant_tile(v4f (&S)[D / 16], const Rec& r, int j, int q
       uint32_t c4 = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = code_of(S[kt][i], gq.r, cr.magic, cr.lo, cr.hi);
+        // symmetric codes need no clamp: |x| / s <= 2^(b-1) - 1 up to one rounding
+        const int c = r.asym ? code_of(S[kt][i], gq.r, cr.magic, cr.lo, cr.hi)
+                             : (int)(f32_bits(fmaf(S[kt][i], gq.r, cr.magic)) & 0xFFu);
         c4 |= (uint32_t)c << (8 * i);
         S[kt][i] = gq.s * ((float)c - fz);
       }
