@@ -7,7 +7,7 @@ and streams only.
 """
 from ._lib import (  # noqa: F401
     LIB, LIB_PATH, EXPORTS, LayerConfig, PaceError, layout, head_alloc, decode_step,
-    flush_requant, prefill_chunk, prefill_workspace_bytes, bf16_decode_step,
+    flush_requant, prefill_chunk, prefill_workspace_bytes, bf16_decode_step, calibrate_heads,
     prepare_decode_step, prepare_bf16_decode_step, prepare_prefill_chunk,
     PACE_OK, PACE_EINVAL, PACE_EUNSUPPORTED, PACE_EHIP,
 )

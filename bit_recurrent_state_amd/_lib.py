@@ -41,8 +41,9 @@ class _Info(ctypes.Structure):
                 ("buffer_bits_actual", ctypes.c_double)]
 
 
-EXPORTS = ["pace_layout", "pace_head_alloc", "pace_prefill_chunk", "pace_prefill_workspace_bytes",
-           "pace_decode_step", "pace_flush_requant", "pace_bf16_decode_step", "pace_status_str"]
+EXPORTS = ["pace_layout", "pace_head_alloc", "pace_calibrate_heads", "pace_prefill_chunk",
+           "pace_prefill_workspace_bytes", "pace_decode_step", "pace_flush_requant",
+           "pace_bf16_decode_step", "pace_status_str"]
 
 
 def _load():
@@ -61,10 +62,11 @@ def _load():
     lib.pace_decode_step.argtypes = [C, P, P, P, P, P, P, P, P, P, P]
     lib.pace_flush_requant.argtypes = [C, P, P, P, P]
     lib.pace_bf16_decode_step.argtypes = [C, P, P, P, P, P, P, P, P]
+    lib.pace_calibrate_heads.argtypes = [C, P, P, P, P, ctypes.c_int32, P, P, P]
     lib.pace_status_str.argtypes = [ctypes.c_int]
     lib.pace_status_str.restype = ctypes.c_char_p
     for name in ["pace_layout", "pace_head_alloc", "pace_prefill_chunk", "pace_decode_step",
-                 "pace_flush_requant", "pace_bf16_decode_step"]:
+                 "pace_flush_requant", "pace_bf16_decode_step", "pace_calibrate_heads"]:
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -212,6 +214,23 @@ def prefill_chunk(cfg: LayerConfig, state, q, k, v, a, beta, o, workspace=None, 
         _ptr(beta, "beta", torch.float32, cfg.B * T * cfg.Hv), T,
         _ptr(o, "o", io, cfg.B * T * cfg.Hv * cfg.dv), ws, wsb, _stream(stream))
     _check(st, "pace_prefill_chunk")
+
+
+def calibrate_heads(cfg: LayerConfig, k, v, a, beta, stream=None):
+    """pace_calibrate_heads.  k [B, T, Hk, dk], v [B, T, Hv, dv] (io dtype), a, beta
+    [B, T, Hv] fp32, all on the device.  Returns (e_h, a_h): fp64 device tensors [Hv]."""
+    import torch
+    T = a.shape[1]
+    io = _io(cfg)
+    c = cfg._c()
+    e_h = torch.empty(cfg.Hv, dtype=torch.float64, device=a.device)
+    a_h = torch.empty(cfg.Hv, dtype=torch.float64, device=a.device)
+    st = LIB.pace_calibrate_heads(
+        ctypes.byref(c), _ptr(k, "k", io, cfg.B * T * cfg.Hk * cfg.dk), _ptr(v, "v", io, cfg.B * T * cfg.Hv * cfg.dv),
+        _ptr(a, "a", torch.float32, cfg.B * T * cfg.Hv), _ptr(beta, "beta", torch.float32, cfg.B * T * cfg.Hv), T,
+        _ptr(e_h, "e_h", torch.float64, cfg.Hv), _ptr(a_h, "a_h", torch.float64, cfg.Hv), _stream(stream))
+    _check(st, "pace_calibrate_heads")
+    return e_h, a_h
 
 
 def prepare_prefill_chunk(cfg: LayerConfig, state, q, k, v, a, beta, o, workspace=None, stream=None):

@@ -1,6 +1,7 @@
 """Build libpace.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-    python -m bit_recurrent_state_amd.build        # or build() from Python
+    python bit_recurrent_state_amd/build.py        # (a script: importing the package
+                                                   #  would load the library first)
 
 Every source is compiled each call (objects go to _build/, the library next to this
 file), in parallel.  Packed-FP32 instruction selection is switched off for all device
@@ -21,7 +22,7 @@ LIB = os.path.join(HERE, "libpace.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["pace_host.cpp", "pace_decode.hip", "pace_prefill.hip", "pace_baseline.hip"]
+SOURCES = ["pace_host.cpp", "pace_decode.hip", "pace_prefill.hip", "pace_baseline.hip", "pace_calib.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

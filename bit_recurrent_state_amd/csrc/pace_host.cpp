@@ -224,6 +224,23 @@ pace_status pace_prefill_chunk(const pace_layer_cfg* cfg, void* state, const voi
   return e == hipSuccess ? PACE_OK : PACE_EHIP;
 }
 
+pace_status pace_calibrate_heads(const pace_layer_cfg* cfg, const void* k, const void* v,
+                                 const float* a, const float* beta, int32_t T,
+                                 double* e_h, double* a_h, void* stream) {
+  const pace_status st = validate(cfg);
+  if (st != PACE_OK) return st;
+  if (T <= 0 || !k || !v || !a || !beta || !e_h || !a_h) return PACE_EINVAL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(a, 4) || !aligned(beta, 4) ||
+      !aligned(e_h, 8) || !aligned(a_h, 8))
+    return PACE_EINVAL;
+  CalibParams p{};
+  p.k = k; p.v = v; p.a = a; p.beta = beta; p.e_h = e_h; p.a_h = a_h;
+  p.B = cfg->B; p.Hv = cfg->Hv; p.Hk = cfg->Hk; p.gamma = cfg->Hv / cfg->Hk;
+  p.T = T; p.dP = cfg->dP; p.group = cfg->group; p.asym = cfg->state_kind == PACE_STATE_ASYM;
+  const hipError_t e = launch_calib(p, cfg->dk, cfg->io_dtype == PACE_IO_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? PACE_OK : PACE_EHIP;
+}
+
 pace_status pace_bf16_decode_step(const pace_layer_cfg* cfg, void* state_bf16, const void* q,
                                   const void* k, const void* v, const float* a,
                                   const float* beta, void* o, void* stream) {

@@ -107,6 +107,16 @@ struct Bf16Params {
   int32_t B, Hv, Hk, gamma;
 };
 
+struct CalibParams {
+  const void* k;
+  const void* v;
+  const float* a;
+  const float* beta;
+  double* e_h;          // [Hv] mean rounding error energy
+  double* a_h;          // [Hv] mean decay
+  int32_t B, Hv, Hk, gamma, T, dP, group, asym;
+};
+
 // Launchers (defined next to their kernels).  They only enqueue work.
 hipError_t launch_decode(const DecodeParams& p, int dk, int dv, int buf_kind, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dk, int dv, int io_bf16,
@@ -114,5 +124,6 @@ hipError_t launch_prefill(const PrefillParams& p, int dk, int dv, int io_bf16,
 size_t prefill_workspace_bytes(int B, int Hv, int dk, int dv, int T, int chunk);
 hipError_t launch_bf16_decode(const Bf16Params& p, int dk, int dv, int io_bf16,
                               hipStream_t stream);
+hipError_t launch_calib(const CalibParams& p, int dk, int io_bf16, hipStream_t stream);
 
 }  // namespace pace

@@ -176,6 +176,22 @@ pace_status pace_layout(const pace_layer_cfg* cfg, pace_layout_info* out);
 pace_status pace_head_alloc(int32_t Hv, int32_t dP, const double* e_h, const double* a_h,
                             int32_t n_8bit, int8_t* head_bits_out, double* E_out);
 
+/* Offline calibration of the head ranking inputs ([p1] "How it differs": e_h is the error
+ * energy one rounding leaves, a_h the head's decay; [p2] "Method": head-level precision
+ * allocation).  For each value head h, runs the exact recurrence from S = 0 over the T
+ * tokens of each of the B sequences and, at every dP-th token, adds the squared Frobenius
+ * error of one rounding of S by the layer's 4-bit quantiser (key groups of cfg->group,
+ * bf16 scales rounded up, symmetric or asymmetric per cfg->state_kind).
+ * In : k [B][T][Hk][dk], v [B][T][Hv][dv] (io_dtype), a, beta [B][T][Hv] fp32 (device).
+ * Out: e_h[Hv] = mean energy over all rounding points of all sequences (0 if T < dP),
+ *      a_h[Hv] = mean a_t over all tokens and sequences; fp64, device memory.
+ * Feed the host copies to pace_head_alloc.  Deterministic (one workgroup per head).
+ * Errors: as pace_prefill_chunk for the configuration; PACE_EINVAL for T < 1 or a null
+ * pointer.  `stream` is a hipStream_t (NULL = default stream). */
+pace_status pace_calibrate_heads(const pace_layer_cfg* cfg, const void* k, const void* v,
+                                 const float* a, const float* beta, int32_t T,
+                                 double* e_h, double* a_h, void* stream);
+
 /* Chunked prefill ([p1] "How it works": the prefill rounding period is the chunk
  * length, 256 tokens; [p3] "Two observations": chunked kernels update the state once
  * per chunk).  Consumes T >= 1 tokens of all B sequences starting from `state`, writes
