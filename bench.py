@@ -203,23 +203,39 @@ def copy_ceiling(torch, nbytes=1 << 30, reps=5):
     return gbs
 
 
-def make_cfg(pace, args, B):
+def head_map(torch, pace, args, layer):
+    """PACE-4/8 head map of one layer: e_h, a_h from a seeded 512-token calibration run on
+    the GPU (pace_calibrate_heads, asymmetric 4-bit quantiser with 32-key groups), then the
+    quarter of heads with the largest E_h at 8 bits (pace_head_alloc)."""
+    d, Hv, Hk, dP = args.dim, args.heads, args.kv_heads, args.dP
+    Bc = 2
+    ccfg = pace.LayerConfig(B=Bc, Hv=Hv, Hk=Hk, dk=d, dv=d, group=32, asym=True, buf="int8",
+                            bf16_io=True, dP=dP)
+    q, k, v, a, beta = make_layer_inputs(torch, Bc, 512, Hv, Hk, d, 100000 + 1000 * (args.seed + 101) + layer,
+                                         timeline=512)
+    e_h, a_h = pace.calibrate_heads(ccfg, k, v, a, beta)
+    bits, _ = pace.head_alloc(e_h.cpu().numpy(), a_h.cpu().numpy(), dP, int(Hv / 4 + 0.5))
+    return [int(x) for x in bits]
+
+
+def make_cfgs(torch, pace, args, B):
+    """One layer configuration per layer (PACE-4/8 layers differ in their head maps)."""
     d, Hv, Hk, dP = args.dim, args.heads, args.kv_heads, args.dP
     if args.variant == "pace4":
-        return pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP)
-    # head map: a quarter of the heads at 8 bits (a fixed map: any map with the same count
-    # moves the same bytes; the E_h ranking itself is pace_head_alloc's, tested separately)
-    hb = [8 if h % 4 == 0 else 4 for h in range(Hv)]
-    return pace.pace48(hb, B=B, Hv=Hv, Hk=Hk, d=d, dP=dP, buf="int8" if args.variant == "pace48-int8" else "mixed")
+        return [pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP)] * args.layers
+    buf = "int8" if args.variant == "pace48-int8" else "mixed"
+    return [pace.pace48(head_map(torch, pace, args, l), B=B, Hv=Hv, Hk=Hk, d=d, dP=dP, buf=buf)
+            for l in range(args.layers)]
 
 
-def build_layers(torch, pace, args, cfg):
+def build_layers(torch, pace, args, cfgs):
     """Per layer: a zeroed state and buffer, the context written by pace_prefill_chunk,
     and dP decode tokens."""
-    B, Hv, Hk, d, dP = cfg.B, cfg.Hv, cfg.Hk, cfg.dk, cfg.dP
-    L = pace.layout(cfg)
     layers = []
     for l in range(args.layers):
+        cfg = cfgs[l]
+        B, Hv, Hk, d, dP = cfg.B, cfg.Hv, cfg.Hk, cfg.dk, cfg.dP
+        L = pace.layout(cfg)
         st = torch.zeros(L["state_bytes"], dtype=torch.uint8, device="cuda")
         bu = torch.zeros(L["buffer_bytes"], dtype=torch.uint8, device="cuda")
         ctx = make_layer_inputs(torch, B, args.context + dP, Hv, Hk, d, 1000 * args.seed + l)
@@ -230,7 +246,7 @@ def build_layers(torch, pace, args, cfg):
         pace.prefill_chunk(cfg, st, pq, pk_, pv, pa, pb, o_ctx, workspace=ws)
         toks = [tuple(x[:, args.context + t].contiguous() for x in ctx) for t in range(dP)]
         o = torch.empty((B, Hv, d), dtype=torch.bfloat16, device="cuda")
-        layers.append(dict(state=st, buf=bu, toks=toks, o=o))
+        layers.append(dict(cfg=cfg, state=st, buf=bu, toks=toks, o=o))
         del ctx, o_ctx, pq, pk_, pv, pa, pb, ws
     torch.cuda.synchronize()
     return layers, L
@@ -238,16 +254,17 @@ def build_layers(torch, pace, args, cfg):
 
 def run_decode(torch, pace, args, B, steps, warmup, split=False):
     """Decode periods of the L-layer stack at batch B.  Returns a dict of figures."""
-    cfg = make_cfg(pace, args, B)
-    dP, Lyr = cfg.dP, args.layers
     t0 = time.time()
-    layers, L = build_layers(torch, pace, args, cfg)
+    cfgs = make_cfgs(torch, pace, args, B)
+    cfg = cfgs[0]
+    dP, Lyr = cfg.dP, args.layers
+    layers, L = build_layers(torch, pace, args, cfgs)
     stream = torch.cuda.Stream()
     calls = []
     for t in range(dP):
         for ly in layers:
             q, k, v, a, b_ = ly["toks"][t]
-            calls.append(pace.prepare_decode_step(cfg, ly["state"], ly["buf"], q, k, v, a, b_, ly["o"], stream=stream))
+            calls.append(pace.prepare_decode_step(ly["cfg"], ly["state"], ly["buf"], q, k, v, a, b_, ly["o"], stream=stream))
     ms = time_graph(torch, stream, calls, steps, warmup)
     n_launch = len(calls) * steps
     launch_s = ms / 1e3 / n_launch                       # mean launch duration in the timed region
@@ -378,7 +395,9 @@ def main():
 
     torch.cuda.set_device(0)
     B, Hv, Hk, d, dP, Lyr = args.batch, args.heads, args.kv_heads, args.dim, args.dP, args.layers
-    cfg0 = make_cfg(pace, args, B)
+    cfg0 = pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP) if args.variant == "pace4" else \
+        pace.pace48([8] * (Hv // 4) + [4] * (Hv - Hv // 4), B=B, Hv=Hv, Hk=Hk, d=d, dP=dP,
+                    buf="int8" if args.variant == "pace48-int8" else "mixed")
     L0 = pace.layout(cfg0)
     log(f"variant {args.variant} B={B} Hv={Hv} Hk={Hk} d={d} dP={dP} layers={Lyr} "
         f"state/layer {L0['state_bytes'] / 1e6:.1f} MB buffer/layer {L0['buffer_bytes'] / 1e6:.1f} MB")
@@ -403,7 +422,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 state / int8 buffer / bf16 io, fp32 + int32 accumulate",
+        "dtype": {"pace4": "int4 state / int8 buffer / bf16 io, fp32 + int32 accumulate",
+                  "pace48-int8": "int4 + int8 (quarter of heads) state / int8 buffer / bf16 io, fp32 + int32 accumulate",
+                  "pace48-mixed": "int4 + int8 (quarter of heads) state / 4-bit key + bf16 value buffer / bf16 io, "
+                                  "fp32 + int32 accumulate"}[args.variant],
         "data": "synthetic (seeded; column-outlier value channels)",
         "config": {"workload": f"{args.variant} decode, {Lyr} gated-delta layers x {Hv} value heads "
                                f"({Hk} key heads), d={d}, B={B}, dP={dP}, {args.context}-token context; "
