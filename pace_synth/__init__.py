@@ -35,10 +35,10 @@ __all__ = [
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """float32 values rounded to the nearest bf16 value (ties to even), as float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    u = (u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)
-    return u.astype(np.uint32).view(np.float32)
+    u = x.view(np.uint32)
+    # finite patterns stay below 2^32 after the increment (at most 0xFF807FFF)
+    u = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return u.view(np.float32)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -111,6 +111,28 @@ def make_tokens(seed: int, B: int, T: int, Hv: int, Hk: int, dk: int, dv: int,
     if bf16:
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     return TokenInputs(q, k, v, a.astype(f32), beta.astype(f32), chans)
+
+
+def make_tokens_chunk(seed: int, chunk: int, B: int, T: int, Hv: int, Hk: int, dk: int, dv: int,
+                      bf16: bool = False) -> TokenInputs:
+    """Chunk `chunk` (T tokens) of a long seeded token stream, generated on its own
+    (seed sequence [seed, chunk]) so that streams of any length fit in memory; same
+    distributions and draw order as make_tokens without outlier channels."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, chunk])))
+    q = rng.standard_normal((B, T, Hk, dk))
+    k = rng.standard_normal((B, T, Hk, dk))
+    v = rng.standard_normal((B, T, Hv, dv))
+    gate_logit = rng.normal(-4.0, 1.0, size=(B, T, Hv))
+    beta_logit = rng.standard_normal((B, T, Hv))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    a = np.exp(-_softplus(gate_logit))
+    beta = 1.0 / (1.0 + np.exp(-beta_logit))
+    f32 = np.float32
+    q, k, v = q.astype(f32), k.astype(f32), v.astype(f32)
+    if bf16:
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return TokenInputs(q, k, v, a.astype(f32), beta.astype(f32), None)
 
 
 def random_packed_state_parts(seed: int, B: int, Hv: int, dk: int, dv: int, group: int,

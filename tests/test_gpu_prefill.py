@@ -109,6 +109,58 @@ def test_prefill_long_shape_first_chunk_sampled():
     check_prefill_call(ocfg, gcfg, zero, toks.span(0, 256), tiles, "long/first-chunk")
 
 
+def test_long_prefill_full_size():
+    """The long-prefill workload at its full size (4 sequences x 32,768 tokens, 32 value /
+    16 key heads, d = 128, bf16, int4 g = 64, 128 chunks) in the launch configuration the
+    benchmark times (one call over all tokens).  Properties that hold at any size:
+      * the one call equals 128 successive one-chunk calls, bit for bit (outputs and the
+        packed state), so it rounds exactly once per chunk from its own rounded state;
+      * sampled tiles, at sampled chunks (first, second, middle, last), match the oracle
+        running its own trajectory chunk by chunk (GPU started from the oracle's packed
+        state of that chunk, compared by the parity protocol)."""
+    from pace_synth import make_tokens_chunk
+    B, Hv, Hk, d, C, NC = 4, 32, 16, 128, 256, 128
+    T = C * NC
+    ocfg = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, asym=False, buf="int8", dP=8, bf16_io=True)
+    gcfg = _lib().LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, bf16_io=True)
+    pace = _lib()
+    print("[long prefill full size] generating inputs", flush=True)
+    chunks = []
+    for c in range(NC):
+        chunks.append(make_tokens_chunk(44, c, B, C, Hv, Hk, d, d, bf16=True))
+        if c % 32 == 31:
+            print(f"[long prefill full size] {c + 1} chunks generated", flush=True)
+    dev_chunks = [tuple(io_dev(x, True) if i < 3 else dev(x) for i, x in enumerate(ch.span(0, C)))
+                  for ch in chunks]
+    full = [torch.cat([dc[i] for dc in dev_chunks], dim=1) for i in range(5)]
+    L = pace.layout(gcfg)
+    zero = torch.zeros(L["state_bytes"], dtype=torch.uint8, device="cuda")
+    o_all = torch.empty((B, T, Hv, d), dtype=torch.bfloat16, device="cuda")
+    st_all = zero.clone()
+    print("[long prefill full size] one call over all tokens", flush=True)
+    pace.prefill_chunk(gcfg, st_all, *full, o_all)
+    st = zero.clone()
+    o_c = torch.empty((B, C, Hv, d), dtype=torch.bfloat16, device="cuda")
+    print("[long prefill full size] chunk-by-chunk calls", flush=True)
+    for c in range(NC):
+        pace.prefill_chunk(gcfg, st, *dev_chunks[c], o_c)
+        assert torch.equal(o_c, o_all[:, C * c:C * (c + 1)]), f"outputs of chunk {c} differ"
+    torch.cuda.synchronize()
+    assert torch.equal(st, st_all), "packed state after the one call differs from chunk-by-chunk"
+    del full, o_all, dev_chunks
+    print("[long prefill full size] oracle trajectory on sampled tiles", flush=True)
+    tiles = [(0, 0), (1, 7), (2, 16), (3, 31)]
+    state = np.zeros(pk.state_layout(ocfg)[2], dtype=np.uint8)
+    for c in range(NC):
+        span = chunks[c].span(0, C)
+        if c % 32 == 0:
+            print(f"[long prefill full size] oracle at chunk {c}", flush=True)
+        if c in (0, 1, NC // 2, NC - 1):
+            state = check_prefill_call(ocfg, gcfg, state, span, tiles, f"long/chunk{c}")
+        else:
+            _, state, _ = pk.prefill_layer(ocfg, state, *span, tiles=tiles)
+
+
 def test_tiny_reference_end_to_end():
     """Tiny reference: B = 2, 4 heads, d = 64, fp32, sym int4 g = 32, int8 buffer,
     512-token prompt (2 chunks) then 64 decode tokens (8 flushes).  Every GPU call
