@@ -133,6 +133,64 @@ def test_decode_step_matches_oracle(name):
     check_states(ocfg, s_gpu, state, pre, tiles, name)
 
 
+FULL = {
+    # name: (B, Hv, Hk, d, group, asym, buf, head_bits) -- the benchmark's layer shapes
+    "pace4_b64": (64, 32, 16, 128, 64, False, "int8", None),
+    "pace4_b128": (128, 32, 16, 128, 64, False, "int8", None),
+    "pace48_int8_b64": (64, 32, 16, 128, 32, True, "int8", "quarter"),
+    "pace48_mixed_b64": (64, 32, 16, 128, 32, True, "mixed", "quarter"),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_decode_full_size_sampled(name):
+    """One pace_decode_step at the benchmark's full layer size (grid of 32 value heads x B
+    sequences, bf16, dP = 8) with random per-sequence counts.  Sampled tiles (both value
+    heads of a key head, flushing and appending sequences) are compared with the oracle;
+    every tile's count is checked against the rule count' = count + 1, or 0 on a flush."""
+    print(f"[decode full size] case={name}", flush=True)
+    B, Hv, Hk, d, g, asym, buf, hb = FULL[name]
+    if hb == "quarter":
+        hb = [8 if h % 4 == 1 else 4 for h in range(Hv)]
+    dP = 8
+    ocfg = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=g, asym=asym, buf=buf, dP=dP,
+                       bf16_io=True, head_bits=hb)
+    gcfg = _lib().LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=g, asym=asym, buf=buf,
+                              bf16_io=True, dP=dP, head_bits=hb)
+    seed = 500 + len(name)
+    bits = [ocfg.bits(h) for h in range(Hv)]
+    state = pk.pack_state(ocfg, pk.state_from_parts(ocfg, random_packed_state_parts(seed, B, Hv, d, d, g, bits, asym)))
+    counts = np.random.default_rng(seed + 7).integers(0, dP, size=B)
+    counts[::5] = dP - 1                               # a fifth of the sequences flush
+    buffer = pk.pack_buffer(ocfg, random_buffer_parts(seed + 1, B, Hv, Hk, d, d, dP, buf == "mixed", counts=counts))
+    toks = make_tokens(seed + 2, B, 1, Hv, Hk, d, d, bf16=True)
+    seqs = [0, 1, 2, B // 2, B // 2 + 3, B - 1]
+    tiles = [(b, h) for b in seqs for h in (0, 1, 14, 15, Hv - 2, Hv - 1)]
+    o_ref, s_ref, b_ref, pre = pk.decode_step_layer(ocfg, state, buffer, *toks.token(0), tiles=tiles)
+    o_gpu, s_gpu, b_gpu = run_gpu_decode(gcfg, state, buffer, toks)
+    parity.check_outputs(o_gpu, o_ref, tiles, name, out_bf16=True)
+    assert len(pre) > 0
+    qg = pk.unpack_state(ocfg, s_gpu, list(pre.keys()))
+    parity.check_flushed_tiles(pre, qg, name)
+    dg, dr = pk.unpack_buffer(ocfg, b_gpu), pk.unpack_buffer(ocfg, b_ref)
+    for b, h in tiles:
+        n = int(dr["count"][b, h])
+        assert dg["count"][b, h] == n
+        kh = h // ocfg.gamma
+        for key in ("a", "beta"):
+            assert np.array_equal(dg[key][b, h, :n], dr[key][b, h, :n]), key
+        assert np.array_equal(dg["kc"][b, kh, :n], dr["kc"][b, kh, :n]), f"k codes (b={b},kh={kh})"
+        assert np.array_equal(dg["ks"][b, kh, :n], dr["ks"][b, kh, :n]), "k scales"
+        if buf == "int8":
+            assert np.array_equal(dg["vc"][b, h, :n], dr["vc"][b, h, :n]), "v codes"
+            assert np.array_equal(dg["vs"][b, h, :n], dr["vs"][b, h, :n]), "v scales"
+        else:
+            assert np.array_equal(dg["v"][b, h, :n], dr["v"][b, h, :n]), "bf16 v"
+    old = np.repeat(np.asarray(counts)[:, None], Hv, axis=1)
+    want = np.where(old + 1 >= dP, 0, old + 1)
+    assert np.array_equal(dg["count"], want), "count rule violated"
+
+
 def test_decode_inactive_sequences_untouched():
     print("[decode parity] active mask", flush=True)
     ocfg, gcfg, state, buffer, toks = make_case("pace4_g64_int8", seed=7)
