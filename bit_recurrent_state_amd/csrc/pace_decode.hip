@@ -124,9 +124,9 @@ struct alignas(16) Smem {
 // GT: scale-group size (32 or 64), 0 = taken from the parameters at run time.
 // AS: 0 = symmetric, 1 = asymmetric, 2 = taken from the parameters at run time.
 template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS>
-// Eight resident workgroups per CU (four waves per SIMD) for the dP <= 8 variants, so a
-// 2048-tile launch runs in one round: at most 128 VGPRs.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOK <= 8 ? 4 : 1)))
+// Eight resident workgroups per CU (four waves per SIMD) for the specialised dP <= 8
+// variants, so a 2048-tile launch runs in one round: at most 128 VGPRs.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOK <= 8 && GT != 0 ? 4 : 1)))
 void decode_kernel(DecodeParams p) {
   using SM = Smem<D, TOK>;
   constexpr int NV = SM::NV;
@@ -493,7 +493,12 @@ void decode_kernel(DecodeParams p) {
           int z = (int)sm.zeros[c * NG + g];
           if (is8) z -= 128;              // the A operand held codes - 128
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) proj[nt][i] += (float)(acc[nt][i] - z * zacc[nt][g][0]) * sc;
+          for (int nt = 0; nt < NT; ++nt) {
+            int ksg = 0;                    // (static selects: g may be a run-time value)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) ksg = gg == g ? zacc[nt][gg][0] : ksg;
+            proj[nt][i] += (float)(acc[nt][i] - z * ksg) * sc;
+          }
         } else {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) proj[nt][i] += (float)acc[nt][i] * sc;
@@ -501,7 +506,14 @@ void decode_kernel(DecodeParams p) {
       }
       if (g + 1 < NG) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = asym ? v4i{0, 0, 0, 0} : zacc[nt][(g + 1) & 3];
+        for (int nt = 0; nt < NT; ++nt) {
+          v4i nx = v4i{0, 0, 0, 0};
+          if (!asym) {
+#pragma unroll
+            for (int gg = 1; gg < 4; ++gg) nx = gg == g + 1 ? zacc[nt][gg] : nx;
+          }
+          acc[nt] = nx;
+        }
       }
     }
 #pragma unroll
@@ -525,7 +537,13 @@ void decode_kernel(DecodeParams p) {
     float yq = sm.pw.P[QS][j] + sm.pw.P[QS + 1][j] + sm.pw.P[QS + 2][j];
 #pragma unroll
     for (int i = 0; i < TOK; ++i) {
-      if (i >= n) break;
+      // (an early exit keeps the short periods cheap; the long-period instantiations keep
+      // a plain guard, which the compiler still unrolls, so nothing is indexed at run time)
+      if constexpr (TOK <= 8) {
+        if (i >= n) break;
+      } else {
+        if (i >= n) continue;
+      }
       const float ai = sm.ga[i];
       const float vh = BUF == PACE_BUF_INT8 ? (float)sm.v.c[i][j] * sm.vs[i] : bf16_to_f32(sm.v.b[i][j]);
       const float ui = sm.gb[i] * (vh - ai * y[i]);
