@@ -14,9 +14,12 @@
 // MFMA with U kept in accumulators.
 //   O = diag(Gamma) Q S + (lower-incl [e^{g_t - g_i} q_t . k_i]) U
 //   S' = Gamma_end S + K^T diag(e^{g_end - g}) U
-// which is the token loop's result exactly in real arithmetic.  Every contraction runs on
-// v_mfma_f32_16x16x4_f32 (fp32 operands, fp32 accumulation: the state must stay accurate
-// to ~1e-5 relative for the rounding decisions at the chunk end).
+// which is the token loop's result exactly in real arithmetic.  The state must stay
+// accurate to ~1e-5 relative for the rounding decisions at the chunk end, so every
+// contraction is fp32-accurate: with bf16 inputs, K K^T and Q K^T are single bf16 MFMA
+// passes (exact products), K S, Q S and K^T (decayed U) take the fp32 operand as three
+// bf16 pieces (v_mfma_f32_16x16x32_bf16), and the small P U and solve products use
+// v_mfma_f32_16x16x4_f32; with fp32 inputs everything uses the fp32 MFMA.
 //
 // One workgroup (4 wave64s) per (sequence, value head).  The state S lives in the MFMA
 // accumulators for the whole call: wave w owns value columns [w D/4, (w+1) D/4), all keys;
@@ -163,18 +166,73 @@ __device__ inline void put8(float* dst, uint4 w) {
   }
 }
 
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v8f __attribute__((ext_vector_type(8)));
+
+__device__ inline v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight fp32 values as three bf16 pieces whose sum is the value to ~2^-24 relative
+// (each piece rounds the remainder of the previous ones to nearest).
+__device__ inline void split3(v8f x, v8bf& p0, v8bf& p1, v8bf& p2) {
+  p0 = __builtin_convertvector(x, v8bf);
+  x -= __builtin_convertvector(p0, v8f);
+  p1 = __builtin_convertvector(x, v8bf);
+  x -= __builtin_convertvector(p1, v8f);
+  p2 = __builtin_convertvector(x, v8bf);
+}
+
+// Two groups of four consecutive bf16 (8 bytes each) as one MFMA operand.
+__device__ inline v8bf load_2x4(const uint16_t* lo, const uint16_t* hi) {
+  const uint2 a = *(const uint2*)lo, b = *(const uint2*)hi;
+  const uint4 w = make_uint4(a.x, a.y, b.x, b.y);
+  v8bf r;
+  __builtin_memcpy(&r, &w, 16);
+  return r;
+}
+
+__device__ inline v8bf load_8(const uint16_t* p) {
+  const uint4 w = *(const uint4*)p;
+  v8bf r;
+  __builtin_memcpy(&r, &w, 16);
+  return r;
+}
+
+// Operand tiles of one sub-block: fp32 (fp32 inputs, fp32 MFMA) or the bf16 inputs as
+// they are, plus the keys transposed (bf16 MFMA).
+template <int D, int IO>
+struct Operands;
+
 template <int D>
+struct Operands<D, 0> {
+  static constexpr int LD = D + 4;
+  float K[kSB][LD];
+  float Q[kSB][LD];
+  float V[kSB][LD];
+};
+
+template <int D>
+struct Operands<D, 1> {
+  static constexpr int LD = D + 8;     // bf16 row stride: 16-byte aligned rows
+  static constexpr int LT = kSB + 8;
+  uint16_t K[kSB][LD];
+  uint16_t Q[kSB][LD];
+  uint16_t V[kSB][LD];
+  uint16_t Kt[D][LT];                  // keys, [key][token]
+};
+
+template <int D, int IO>
 struct Smem {
-  static constexpr int LD = D + 4;     // row stride of token-major tiles (floats)
   static constexpr int LA = kSB + 4;
-  float K[kSB][LD];                    // keys of the sub-block
-  float Q[kSB][LD];                    // queries
-  float V[kSB][LD];                    // values
+  Operands<D, IO> x;
   float A[kSB][LA];                    // beta_t e^{g_t-g_i} k_t.k_i, strictly lower
   float Ti[kSB / 16][16][20];          // inverses of the diagonal blocks (I + A_ii)
   float P[kSB][LA];                    // e^{g_t-g_i} q_t.k_i, lower incl. diagonal
   float g[kSB];                        // cumulative log decay
   float beta[kSB];
+  float gam[kSB];                      // e^{g_t}
+  float wend[kSB];                     // e^{g_end - g_t}
 };
 
 template <int D, int IO>
@@ -182,9 +240,9 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
   constexpr int KT = D / 16;           // key tiles
   constexpr int CT = D / 64;           // column tiles per wave
   constexpr int TT = kSB / 16;         // token tiles
-  constexpr int VS = IO == 1 ? 8 : 4;  // floats per 16-byte input vector
+  constexpr int VS = IO == 1 ? 8 : 4;  // elements per 16-byte input vector
   using I = Inputs<D, IO>;
-  __shared__ Smem<D> sm;
+  __shared__ Smem<D, IO> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, qd = lane >> 4;
@@ -252,9 +310,21 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
     for (int it = 0; it < I::NV; ++it) {
       const int i = tid + it * kThreads;
       const int t = i / I::VPR, c = (i % I::VPR) * VS;
-      put8<IO>(&sm.K[t][c], in.k[it]);
-      put8<IO>(&sm.Q[t][c], in.q[it]);
-      put8<IO>(&sm.V[t][c], in.v[it]);
+      if constexpr (IO == 1) {
+        *(uint4*)&sm.x.K[t][c] = in.k[it];
+        *(uint4*)&sm.x.Q[t][c] = in.q[it];
+        *(uint4*)&sm.x.V[t][c] = in.v[it];
+        const uint32_t w[4] = {in.k[it].x, in.k[it].y, in.k[it].z, in.k[it].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sm.x.Kt[c + 2 * e][t] = (uint16_t)(w[e] & 0xFFFFu);
+          sm.x.Kt[c + 2 * e + 1][t] = (uint16_t)(w[e] >> 16);
+        }
+      } else {
+        put8<IO>(&sm.x.K[t][c], in.k[it]);
+        put8<IO>(&sm.x.Q[t][c], in.q[it]);
+        put8<IO>(&sm.x.V[t][c], in.v[it]);
+      }
     }
     if (wave == 0) {
       // inclusive scan of log a over the 64 tokens (a = 0 is clamped to e^-80)
@@ -264,8 +334,11 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
         const float y = __shfl_up(x, o);
         if (lane >= o) x += y;
       }
+      const float gend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
       sm.g[lane] = x;
       sm.beta[lane] = in.beta;
+      sm.gam[lane] = expf(x);
+      sm.wend[lane] = expf(gend - x);
     }
     // prefetch the next sub-block while this one is computed
     if (sb + 1 < nsb) load_inputs<D, IO>(in, p, b, h, kh, t0 + kSB, min(kSB, p.T - t0 - kSB), tid);
@@ -279,16 +352,23 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
       int ti = 0;
       while (pr > ti) { pr -= ti + 1; ++ti; }
       const int tj = pr;
-      const float(*X)[Smem<D>::LD] = isq ? sm.Q : sm.K;
       v4f acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (IO == 1) {         // exact bf16 inputs: one pass
+        const uint16_t* X = isq ? &sm.x.Q[16 * ti + l16][0] : &sm.x.K[16 * ti + l16][0];
 #pragma unroll
-      for (int v = 0; v < D / 16; ++v) {
-        const float4 xa = *(const float4*)&X[16 * ti + l16][16 * v + 4 * qd];
-        const float4 xb = *(const float4*)&sm.K[16 * tj + l16][16 * v + 4 * qd];
-        acc = mfma4(xa.x, xb.x, acc);
-        acc = mfma4(xa.y, xb.y, acc);
-        acc = mfma4(xa.z, xb.z, acc);
-        acc = mfma4(xa.w, xb.w, acc);
+        for (int kb = 0; kb < D / 32; ++kb)
+          acc = mfma_bf16(load_8(X + 32 * kb + 8 * qd), load_8(&sm.x.K[16 * tj + l16][32 * kb + 8 * qd]), acc);
+      } else {
+        const float* X = isq ? &sm.x.Q[16 * ti + l16][0] : &sm.x.K[16 * ti + l16][0];
+#pragma unroll
+        for (int v = 0; v < D / 16; ++v) {
+          const float4 xa = *(const float4*)(X + 16 * v + 4 * qd);
+          const float4 xb = *(const float4*)&sm.x.K[16 * tj + l16][16 * v + 4 * qd];
+          acc = mfma4(xa.x, xb.x, acc);
+          acc = mfma4(xa.y, xb.y, acc);
+          acc = mfma4(xa.z, xb.z, acc);
+          acc = mfma4(xa.w, xb.w, acc);
+        }
       }
       const int i = 16 * tj + l16;
       const float gi = sm.g[i];
@@ -301,7 +381,52 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
       }
     }
 
-    // ------------------------ right-hand sides diag(beta) V - diag(beta Gamma) K S
+    // ------ K S and Q S of the sub-block's starting state (own columns, accumulators)
+    v4f KS[CT][TT], QS[CT][TT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) KS[c][tt] = QS[c][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (IO == 1) {
+      // 32-key blocks: lane group qd feeds keys 32 kb + 4 qd + (0..3) and 32 kb + 16 +
+      // 4 qd + (0..3), i.e. its accumulator entries of key tiles 2 kb and 2 kb + 1; the
+      // state enters as three bf16 pieces, K and Q as they are
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int kb = 0; kb < KT / 2; ++kb) {
+          const v4f s0 = S[c][2 * kb], s1 = S[c][2 * kb + 1];
+          v8bf p0, p1, p2;
+          split3(v8f{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]}, p0, p1, p2);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) {
+            const int row = 16 * tt + l16;
+            const v8bf ak = load_2x4(&sm.x.K[row][32 * kb + 4 * qd], &sm.x.K[row][32 * kb + 16 + 4 * qd]);
+            const v8bf aq = load_2x4(&sm.x.Q[row][32 * kb + 4 * qd], &sm.x.Q[row][32 * kb + 16 + 4 * qd]);
+            KS[c][tt] = mfma_bf16(ak, p0, KS[c][tt]);
+            KS[c][tt] = mfma_bf16(ak, p1, KS[c][tt]);
+            KS[c][tt] = mfma_bf16(ak, p2, KS[c][tt]);
+            QS[c][tt] = mfma_bf16(aq, p0, QS[c][tt]);
+            QS[c][tt] = mfma_bf16(aq, p1, QS[c][tt]);
+            QS[c][tt] = mfma_bf16(aq, p2, QS[c][tt]);
+          }
+        }
+    } else {                           // fp32: K S here, Q S with the outputs
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int row = 16 * tt + l16;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const float4 kx = *(const float4*)&sm.x.K[row][16 * kt + 4 * qd];
+          const float kv[4] = {kx.x, kx.y, kx.z, kx.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < CT; ++c) KS[c][tt] = mfma4(kv[r], S[c][kt][r], KS[c][tt]);
+        }
+      }
+    }
+    // right-hand sides R = diag(beta) V - diag(beta Gamma) K S
     v4f R[CT][TT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
@@ -311,25 +436,11 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * tt + 4 * qd + r;
-          R[c][tt][r] = sm.beta[t] * sm.V[t][j];
+          float vv;
+          if constexpr (IO == 1) vv = bf16_to_f32(sm.x.V[t][j]);
+          else vv = sm.x.V[t][j];
+          R[c][tt][r] = sm.beta[t] * fmaf(-sm.gam[t], KS[c][tt][r], vv);
         }
-    }
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int t = 16 * tt + l16;
-      const float sc = -sm.beta[t] * expf(sm.g[t]);
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const float4 kx = *(const float4*)&sm.K[t][16 * kt + 4 * qd];
-        const float k0 = kx.x * sc, k1 = kx.y * sc, k2 = kx.z * sc, k3 = kx.w * sc;
-#pragma unroll
-        for (int c = 0; c < CT; ++c) {
-          R[c][tt] = mfma4(k0, S[c][kt][0], R[c][tt]);
-          R[c][tt] = mfma4(k1, S[c][kt][1], R[c][tt]);
-          R[c][tt] = mfma4(k2, S[c][kt][2], R[c][tt]);
-          R[c][tt] = mfma4(k3, S[c][kt][3], R[c][tt]);
-        }
-      }
     }
     __syncthreads();     // A and P complete
 
@@ -380,23 +491,23 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
     // ----------------------------- outputs O = diag(Gamma) Q S + P U, own columns
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      v4f O[CT];
-#pragma unroll
-      for (int c = 0; c < CT; ++c) O[c] = v4f{0.f, 0.f, 0.f, 0.f};
       const int tr = 16 * tt + l16;
-      const float gq = expf(sm.g[tr]);
+      v4f O[CT];
+      if constexpr (IO == 0) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const float4 qx = *(const float4*)&sm.Q[tr][16 * kt + 4 * qd];
-        const float q0 = qx.x * gq, q1 = qx.y * gq, q2 = qx.z * gq, q3 = qx.w * gq;
+        for (int kt = 0; kt < KT; ++kt) {
+          const float4 qx = *(const float4*)&sm.x.Q[tr][16 * kt + 4 * qd];
+          const float qv[4] = {qx.x, qx.y, qx.z, qx.w};
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-          O[c] = mfma4(q0, S[c][kt][0], O[c]);
-          O[c] = mfma4(q1, S[c][kt][1], O[c]);
-          O[c] = mfma4(q2, S[c][kt][2], O[c]);
-          O[c] = mfma4(q3, S[c][kt][3], O[c]);
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < CT; ++c) QS[c][tt] = mfma4(qv[r], S[c][kt][r], QS[c][tt]);
         }
       }
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[c][r] = sm.gam[16 * tt + 4 * qd + r] * QS[c][tt][r];
 #pragma unroll
       for (int ib = 0; ib <= tt; ++ib) {
         const float4 px = *(const float4*)&sm.P[tr][16 * ib + 4 * qd];
@@ -424,23 +535,47 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
 
     // --------------------------- state S' = Gamma_end S + K^T diag(e^{g_end - g}) U
     {
-      const float gend = sm.g[kSB - 1];
-      const float ge = expf(gend);
+      const float ge = sm.gam[kSB - 1];
 #pragma unroll
       for (int c = 0; c < CT; ++c)
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) S[c][kt] *= ge;
+      if constexpr (IO == 1) {
+        // 32-token blocks: lane group qd feeds tokens 32 tb + 4 qd + (0..3) and 32 tb +
+        // 16 + 4 qd + (0..3) (its accumulator entries of token tiles 2 tb and 2 tb + 1);
+        // the decayed U enters as three bf16 pieces, the transposed keys as they are
 #pragma unroll
-      for (int tb = 0; tb < TT; ++tb) {
+        for (int c = 0; c < CT; ++c)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int tok = 16 * tb + 4 * qd + s;
-          const float w = expf(gend - sm.g[tok]);
+          for (int tb = 0; tb < TT / 2; ++tb) {
+            const float4 w0 = *(const float4*)&sm.wend[32 * tb + 4 * qd];
+            const float4 w1 = *(const float4*)&sm.wend[32 * tb + 16 + 4 * qd];
+            const v4f u0 = U[c][2 * tb], u1 = U[c][2 * tb + 1];
+            v8bf p0, p1, p2;
+            split3(v8f{u0[0] * w0.x, u0[1] * w0.y, u0[2] * w0.z, u0[3] * w0.w,
+                       u1[0] * w1.x, u1[1] * w1.y, u1[2] * w1.z, u1[3] * w1.w}, p0, p1, p2);
 #pragma unroll
-          for (int kt = 0; kt < KT; ++kt) {
-            const float kv = sm.K[tok][16 * kt + l16] * w;
+            for (int kt = 0; kt < KT; ++kt) {
+              const uint16_t* kr = &sm.x.Kt[16 * kt + l16][0];
+              const v8bf ak = load_2x4(kr + 32 * tb + 4 * qd, kr + 32 * tb + 16 + 4 * qd);
+              S[c][kt] = mfma_bf16(ak, p0, S[c][kt]);
+              S[c][kt] = mfma_bf16(ak, p1, S[c][kt]);
+              S[c][kt] = mfma_bf16(ak, p2, S[c][kt]);
+            }
+          }
+      } else {
 #pragma unroll
-            for (int c = 0; c < CT; ++c) S[c][kt] = mfma4(kv, U[c][tb][s], S[c][kt]);
+        for (int tb = 0; tb < TT; ++tb) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int tok = 16 * tb + 4 * qd + s;
+            const float w = sm.wend[tok];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+              const float kv = sm.x.K[tok][16 * kt + l16] * w;
+#pragma unroll
+              for (int c = 0; c < CT; ++c) S[c][kt] = mfma4(kv, U[c][tb][s], S[c][kt]);
+            }
           }
         }
       }
