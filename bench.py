@@ -284,31 +284,32 @@ def run_decode(torch, pace, args, B, steps, warmup, split=False):
     return res
 
 
-PREFILL_MFMA_PEAK_TFLOPS = 157.3          # MI355X dense fp32 matrix peak
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}     # MI355X dense matrix peaks
 
 
-def prefill_flops(T, Hv, B, d, chunk=256, sb=64):
-    """(algorithmic, executed) flops of pace_prefill_chunk over B x Hv (sequence, head)
+def prefill_flops(T, Hv, B, d, bf16_io=True, chunk=256, sb=64):
+    """Algorithmic and executed flops of pace_prefill_chunk over B x Hv (sequence, head)
     pairs of T tokens.  Algorithmic: the WY form on whole 256-token chunks (72.7 MFLOP per
-    chunk-head at d = 128); executed: the fp32 MFMA work the 64-token sub-block kernel
-    issues (16x16x4 MFMAs, 2048 flops each)."""
+    chunk-head at d = 128, triangular products counted once).  Executed: what the
+    64-token sub-block kernel issues per workgroup and sub-block, by MFMA type -- with bf16
+    inputs, bf16 16x16x32 MFMAs for K K^T and Q K^T (one pass) and for K S, Q S and the
+    state update (three passes each: the fp32 operand as three bf16 pieces), and fp32
+    16x16x4 MFMAs for the blocked solve and P U; with fp32 inputs, all fp32 16x16x4."""
     C = chunk
-    # MACs with triangularity: K K^T and Q K^T (half), W_v and W_k (T lower), P U (half),
-    # U, Q S_0, S_C (full), the unit-triangular inverse (C^3 / 6); 2 flops per MAC
     per_chunk = 2 * (2.5 * C * C * d + 3 * C * d * d + C ** 3 / 6)
-    n_chunks = -(-T // C)
-    alg = per_chunk * n_chunks * B * Hv
-    tt = sb // 16
-    kt = d // 16
+    alg = per_chunk * (-(-T // C)) * B * Hv
+    tt, kt, ct = sb // 16, d // 16, d // 16          # token, key and column tiles
     pairs = tt * (tt + 1) // 2
-    mfma_per_sb = (2 * pairs * (d // 4)          # Gram and query-key tiles
-                   + tt * (d // 16) * 4 * (d // 16)    # K S (all column tiles)
-                   + tt * kt * 4 * (d // 16)           # Q S
-                   + pairs * 4 * (d // 16)             # P U
-                   + tt * 4 * kt * (d // 16))          # S update
-    n_sb = -(-T // sb)
-    executed = mfma_per_sb * 2 * 16 * 16 * 4 * n_sb * B * Hv
-    return alg, executed
+    solve_f32 = (sum(4 * ib for ib in range(tt)) + 4 * tt) * ct
+    pu_f32 = pairs * 4 * ct
+    if bf16_io:
+        bf16 = 2 * pairs * (d // 32) + 2 * 3 * (kt // 2) * tt * ct + 3 * (tt // 2) * kt * ct
+        f32 = solve_f32 + pu_f32
+    else:
+        bf16 = 0
+        f32 = 2 * pairs * (d // 4) + 2 * tt * kt * 4 * ct + solve_f32 + pu_f32 + tt * 4 * kt * ct
+    n = -(-T // sb) * B * Hv
+    return alg, {"bf16": bf16 * 2 * 16 * 16 * 32 * n, "f32": f32 * 2 * 16 * 16 * 4 * n}
 
 
 def run_long_prefill(torch, pace, args):
@@ -337,17 +338,24 @@ def run_long_prefill(torch, pace, args):
         if rep:
             times.append(s.elapsed_time(e))
     ms = float(np.median(times))
-    alg, exe = prefill_flops(T, Hv, B, d)
+    alg, exe = prefill_flops(T, Hv, B, d, bf16_io=True)
+    sec = ms / 1e3
+    util = {k: round(v / sec / 1e12 / MFMA_PEAK_TFLOPS[k], 4) for k, v in exe.items()}
     res = {"workload": f"long chunked prefill B={B} x {T} tokens, {Hv} value / {Hk} key heads, d={d}, bf16 io, "
                        f"int4 g=64 rounded per 256-token chunk",
-           "ms": round(ms, 3), "tokens_per_s": round(B * T / (ms / 1e3), 1),
-           "algorithmic_TFLOP": round(alg / 1e12, 4), "algorithmic_TFLOPs": round(alg / (ms / 1e3) / 1e12, 2),
-           "executed_mfma_TFLOP": round(exe / 1e12, 4), "executed_TFLOPs": round(exe / (ms / 1e3) / 1e12, 2),
-           "mfma_dtype": "fp32 (v_mfma_f32_16x16x4_f32)", "mfma_peak_TFLOPs": PREFILL_MFMA_PEAK_TFLOPS,
-           "mfma_util": round(exe / (ms / 1e3) / 1e12 / PREFILL_MFMA_PEAK_TFLOPS, 4),
+           "ms": round(ms, 3), "tokens_per_s": round(B * T / sec, 1),
+           "algorithmic_TFLOP": round(alg / 1e12, 4), "algorithmic_TFLOPs": round(alg / sec / 1e12, 2),
+           "executed_TFLOP": {k: round(v / 1e12, 4) for k, v in exe.items()},
+           "executed_TFLOPs": {k: round(v / sec / 1e12, 2) for k, v in exe.items()},
+           "mfma_peak_TFLOPs": MFMA_PEAK_TFLOPS,
+           "mfma_util_of_dtype_peak": util,
+           "note": "bf16 figures count the three split passes of the fp32 operands (exact bf16 "
+                   "inputs times the state / decayed U as three bf16 pieces)",
            "workgroups": B * Hv}
-    log(f"long prefill: {ms:.2f} ms, {res['tokens_per_s']:,.0f} tok/s, executed {res['executed_TFLOPs']} TFLOP/s "
-        f"(util {res['mfma_util']:.3f} of fp32 MFMA peak), algorithmic {res['algorithmic_TFLOPs']} TFLOP/s")
+    log(f"long prefill: {ms:.2f} ms, {res['tokens_per_s']:,.0f} tok/s, executed "
+        f"bf16 {res['executed_TFLOPs']['bf16']} TFLOP/s ({util['bf16']:.3f} of peak), "
+        f"f32 {res['executed_TFLOPs']['f32']} TFLOP/s ({util['f32']:.3f} of peak), "
+        f"algorithmic {res['algorithmic_TFLOPs']} TFLOP/s")
     # decode after the prompt: B = 4, one layer
     bu = torch.zeros(L["buffer_bytes"], dtype=torch.uint8, device="cuda")
     od = torch.empty((B, Hv, d), dtype=torch.bfloat16, device="cuda")

@@ -314,12 +314,6 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
         *(uint4*)&sm.x.K[t][c] = in.k[it];
         *(uint4*)&sm.x.Q[t][c] = in.q[it];
         *(uint4*)&sm.x.V[t][c] = in.v[it];
-        const uint32_t w[4] = {in.k[it].x, in.k[it].y, in.k[it].z, in.k[it].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sm.x.Kt[c + 2 * e][t] = (uint16_t)(w[e] & 0xFFFFu);
-          sm.x.Kt[c + 2 * e + 1][t] = (uint16_t)(w[e] >> 16);
-        }
       } else {
         put8<IO>(&sm.x.K[t][c], in.k[it]);
         put8<IO>(&sm.x.Q[t][c], in.q[it]);
@@ -335,49 +329,88 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
         if (lane >= o) x += y;
       }
       const float gend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-      sm.g[lane] = x;
+      sm.g[lane] = x * 1.4426950408889634f;   // log2 units: decays are exp2 of differences
       sm.beta[lane] = in.beta;
       sm.gam[lane] = expf(x);
       sm.wend[lane] = expf(gend - x);
     }
-    // prefetch the next sub-block while this one is computed
-    if (sb + 1 < nsb) load_inputs<D, IO>(in, p, b, h, kh, t0 + kSB, min(kSB, p.T - t0 - kSB), tid);
     __syncthreads();
 
     // ------------------------------------------- Gram and query-key tiles (lower)
-    // jobs: 10 lower-triangular token-tile pairs for K K^T and for Q K^T
-    for (int job = wave; job < 2 * TT * (TT + 1) / 2; job += 4) {
-      const bool isq = job >= TT * (TT + 1) / 2;
-      int pr = isq ? job - TT * (TT + 1) / 2 : job;
-      int ti = 0;
-      while (pr > ti) { pr -= ti + 1; ++ti; }
-      const int tj = pr;
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
+    // 20 jobs (10 lower-triangular token-tile pairs for K K^T and for Q K^T), five per
+    // wave, all issued together; job j of wave w is pair (j / 2) * 4 + w ... in the fixed
+    // order below.
+    {
+      constexpr int NJ = TT * (TT + 1);          // 20
+      constexpr int JPW = NJ / 4;                // 5 per wave
+      v4f acc[JPW];
+      int tis[JPW], tjs[JPW];
+      bool isqs[JPW];
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int job = wave + 4 * jj;
+        const bool isq = job >= NJ / 2;
+        int pr = isq ? job - NJ / 2 : job;
+        int ti = 0;
+        while (pr > ti) { pr -= ti + 1; ++ti; }
+        tis[jj] = ti; tjs[jj] = pr; isqs[jj] = isq;
+        acc[jj] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
       if constexpr (IO == 1) {         // exact bf16 inputs: one pass
-        const uint16_t* X = isq ? &sm.x.Q[16 * ti + l16][0] : &sm.x.K[16 * ti + l16][0];
 #pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb)
-          acc = mfma_bf16(load_8(X + 32 * kb + 8 * qd), load_8(&sm.x.K[16 * tj + l16][32 * kb + 8 * qd]), acc);
+        for (int kb = 0; kb < D / 32; ++kb) {
+          v8bf xa[JPW], xb[JPW];
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj) {
+            const uint16_t* X = isqs[jj] ? &sm.x.Q[16 * tis[jj] + l16][0] : &sm.x.K[16 * tis[jj] + l16][0];
+            xa[jj] = load_8(X + 32 * kb + 8 * qd);
+            xb[jj] = load_8(&sm.x.K[16 * tjs[jj] + l16][32 * kb + 8 * qd]);
+          }
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj) acc[jj] = mfma_bf16(xa[jj], xb[jj], acc[jj]);
+        }
       } else {
-        const float* X = isq ? &sm.x.Q[16 * ti + l16][0] : &sm.x.K[16 * ti + l16][0];
 #pragma unroll
-        for (int v = 0; v < D / 16; ++v) {
-          const float4 xa = *(const float4*)(X + 16 * v + 4 * qd);
-          const float4 xb = *(const float4*)&sm.x.K[16 * tj + l16][16 * v + 4 * qd];
-          acc = mfma4(xa.x, xb.x, acc);
-          acc = mfma4(xa.y, xb.y, acc);
-          acc = mfma4(xa.z, xb.z, acc);
-          acc = mfma4(xa.w, xb.w, acc);
+        for (int jj = 0; jj < JPW; ++jj) {
+          const float* X = isqs[jj] ? &sm.x.Q[16 * tis[jj] + l16][0] : &sm.x.K[16 * tis[jj] + l16][0];
+#pragma unroll
+          for (int v = 0; v < D / 16; ++v) {
+            const float4 xa = *(const float4*)(X + 16 * v + 4 * qd);
+            const float4 xb = *(const float4*)&sm.x.K[16 * tjs[jj] + l16][16 * v + 4 * qd];
+            acc[jj] = mfma4(xa.x, xb.x, acc[jj]);
+            acc[jj] = mfma4(xa.y, xb.y, acc[jj]);
+            acc[jj] = mfma4(xa.z, xb.z, acc[jj]);
+            acc[jj] = mfma4(xa.w, xb.w, acc[jj]);
+          }
         }
       }
-      const int i = 16 * tj + l16;
-      const float gi = sm.g[i];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * ti + 4 * qd + r;
-        const float dec = expf(fminf(sm.g[t] - gi, 0.f));
-        if (isq) sm.P[t][i] = t >= i ? dec * acc[r] : 0.f;
-        else sm.A[t][i] = t > i ? sm.beta[t] * dec * acc[r] : 0.f;
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int i = 16 * tjs[jj] + l16;
+        const float gi = sm.g[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * tis[jj] + 4 * qd + r;
+          const float dec = exp2f(fminf(sm.g[t] - gi, 0.f));
+          if (isqs[jj]) sm.P[t][i] = t >= i ? dec * acc[jj][r] : 0.f;
+          else sm.A[t][i] = t > i ? sm.beta[t] * dec * acc[jj][r] : 0.f;
+        }
+      }
+    }
+    // prefetch the next sub-block while the rest of this one is computed
+    if (sb + 1 < nsb) load_inputs<D, IO>(in, p, b, h, kh, t0 + kSB, min(kSB, p.T - t0 - kSB), tid);
+    if constexpr (IO == 1) {
+      // keys transposed for the state update: thread -> (key, 8-token block); column
+      // reads and one 16-byte row write per pair, both free of bank conflicts
+#pragma unroll
+      for (int it = 0; it < D * (kSB / 8) / kThreads; ++it) {
+        const int pidx = tid + it * kThreads;
+        const int key = pidx % D, blk = pidx / D;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)sm.x.K[8 * blk + 2 * e][key] | ((uint32_t)sm.x.K[8 * blk + 2 * e + 1][key] << 16);
+        *(uint4*)&sm.x.Kt[key][8 * blk] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
 
