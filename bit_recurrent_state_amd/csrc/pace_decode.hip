@@ -111,8 +111,8 @@ struct alignas(16) Smem {
   alignas(16) uint16_t kT[CH][D][8];        // key codes as bf16, rows in (tile, row) order
   alignas(16) float G[NV][NV];              // Gram matrix of the slots (scaled)
   float Gq[NV];                             // k_slot . q (the q pieces combined)
-  alignas(16) float scf[D * 4];             // this tile's scales as fp32, [col][group]
-  alignas(16) uint8_t zeros[D * 4];         // this tile's zero points, one byte each
+  alignas(16) float scf[4][D];              // this tile's scales as fp32, [group][col]
+  alignas(16) uint8_t zeros[4][D];          // this tile's zero points, [group][col], a byte each
   float vscale[NV];                         // key scale of each token slot / q piece scale
   float vs[TOK], ga[TOK], gb[TOK];
   float red[3][4 * kWaves];                 // row maxima of |k|, |v|, |q|
@@ -380,28 +380,32 @@ void decode_kernel(DecodeParams p) {
       *(uint4*)&sm.kc[row][16 * (i % RV)] = make_uint4(0, 0, 0, 0);
   }
   if (tid >= n && tid < NV && (tid < QS || flush_only || tid >= QS + 3)) sm.vscale[tid] = 0.f;
-  if (tid < sc_vec) {                       // 8 bf16 scales -> fp32
+  // scales and zero points regrouped [group][col]: a lane's four output columns of one
+  // group are then one vector read
+  const int lng = NG == 4 ? 2 : NG - 1;      // log2 NG (NG in {1, 2, 4})
+  if (tid < sc_vec) {                       // 8 bf16 scales [col][group] -> fp32
     const uint32_t w[4] = {sc_reg.x, sc_reg.y, sc_reg.z, sc_reg.w};
-    float4* dst = (float4*)&sm.scf[8 * tid];
-    dst[0] = make_float4(bits_f32(w[0] << 16), bits_f32(w[0] & 0xFFFF0000u), bits_f32(w[1] << 16), bits_f32(w[1] & 0xFFFF0000u));
-    dst[1] = make_float4(bits_f32(w[2] << 16), bits_f32(w[2] & 0xFFFF0000u), bits_f32(w[3] << 16), bits_f32(w[3] & 0xFFFF0000u));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int e = 8 * tid + k;
+      const uint32_t u = (k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16);
+      sm.scf[e & (NG - 1)][e >> lng] = bits_f32(u);
+    }
   }
   if (asym && tid < zp_vec) {
-    if (is8) {
-      ((uint4*)sm.zeros)[tid] = zp_reg;
-    } else {                                 // 32 packed 4-bit zero points -> one byte each
-      const uint32_t w[4] = {zp_reg.x, zp_reg.y, zp_reg.z, zp_reg.w};
-      uint32_t o[8];
+    const uint32_t w[4] = {zp_reg.x, zp_reg.y, zp_reg.z, zp_reg.w};
+    if (is8) {                               // 16 zero points, a byte each
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // bytes b0..b3 hold zero points (2i, 2i+1) in (low, high) nibbles
-        const uint32_t lo = w[e] & 0x0F0F0F0Fu, hi = (w[e] >> 4) & 0x0F0F0F0Fu;
-        o[2 * e] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);       // lo0 hi0 lo1 hi1
-        o[2 * e + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // lo2 hi2 lo3 hi3
+      for (int k = 0; k < 16; ++k) {
+        const int e = 16 * tid + k;
+        sm.zeros[e & (NG - 1)][e >> lng] = (uint8_t)(w[k >> 2] >> (8 * (k & 3)));
       }
-      uint4* dst = (uint4*)&sm.zeros[32 * tid];
-      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {                                 // 32 packed 4-bit zero points (low nibble first)
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const int e = 32 * tid + k;
+        sm.zeros[e & (NG - 1)][e >> lng] = (uint8_t)((w[k >> 3] >> (4 * (k & 7))) & 15u);
+      }
     }
   }
   __syncthreads();
@@ -485,19 +489,22 @@ void decode_kernel(DecodeParams p) {
       if ((kb + 1) % kpg != 0) continue;
       // end of scale group g: scale (and an asymmetric zero point) once per (column, group)
       const int g = kb / kpg;
+      const float4 sc4 = *(const float4*)&sm.scf[g][ocol];
+      const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+      const uint32_t z4 = asym ? *(const uint32_t*)&sm.zeros[g][ocol] : 0u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = ocol + i;
-        const float sc = sm.scf[c * NG + g];
+        const float sc = scv[i];
         if (asym) {
-          int z = (int)sm.zeros[c * NG + g];
+          int z = (int)((z4 >> (8 * i)) & 0xFFu);
           if (is8) z -= 128;              // the A operand held codes - 128
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             int ksg = 0;                    // (static selects: g may be a run-time value)
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) ksg = gg == g ? zacc[nt][gg][0] : ksg;
-            proj[nt][i] += (float)(acc[nt][i] - z * ksg) * sc;
+            // |z| <= 255 and |ksg| <= 127 * 64: a 24-bit product
+            proj[nt][i] += (float)(acc[nt][i] - __mul24(z, ksg)) * sc;
           }
         } else {
 #pragma unroll
@@ -621,8 +628,8 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int g = kb / kpg;
-      const float sc = sm.scf[c * NG + g];
-      const int z = asym ? (int)sm.zeros[c * NG + g] : 1 << (bits - 1);
+      const float sc = sm.scf[g][c];
+      const int z = asym ? (int)sm.zeros[g][c] : 1 << (bits - 1);
       const float gs = gn * sc, gz = -gs * (float)z;
       uint32_t b0, b1;            // 4 stored codes each (bytes): keys +0..3, +4..7
       if (!is8) {

@@ -96,10 +96,10 @@ __host__ __device__ inline float rne_quotient(float x, float s, float r) {
     n -= 1.0f;
     e2 += 2.0f * s;
   }
-  // now |x/s - n| <= 1/2; resolve exact ties to even
+  // now |x/s - n| <= 1/2; resolve exact ties to even (n is an integer below 2^24)
   if (e2 == s || e2 == -s) {
     float alt = n + (e2 > 0 ? 1.0f : -1.0f);
-    if (fmodf(n, 2.0f) != 0.0f) n = alt;
+    if ((int)n & 1) n = alt;
   }
   return n;
 }
@@ -123,9 +123,12 @@ __host__ __device__ inline GroupQuant group_quant(float mn, float mx, bool asym,
   } else {
     const float lo = fminf(mn, 0.f), hi = fmaxf(mx, 0.f);
     // hi - lo rounded up to fp32 keeps the ceiling exact: the scale only moves up when
-    // the exact range lies above its fp32 rounding
-    float range = hi - lo;
-    if ((double)range < (double)hi - (double)lo) range = bits_f32(f32_bits(range) + 1u);
+    // the exact range lies above its fp32 rounding.  hi >= 0 >= lo, so with a = the
+    // larger and b = the smaller of hi and -lo, the rounding error of a + b is
+    // b - (range - a), exactly (Dekker's fast two-sum).
+    const float a = fmaxf(hi, -lo), b = fminf(hi, -lo);
+    float range = a + b;
+    if (b - (range - a) > 0.f) range = bits_f32(f32_bits(range) + 1u);
     q.s = bf16_ceil_div(range, (float)levels, bits == 8 ? 1.0f / 255.0f : 1.0f / 15.0f);
     q.z = q.s > 0.f ? (int)fminf(fmaxf(rne_quotient(-lo, q.s, 1.0f / q.s), 0.f), (float)levels) : 0;
   }

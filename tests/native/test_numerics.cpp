@@ -127,6 +127,23 @@ int main() {
     EXPECT(g4.s == ref_bf16_ceil(3.0 / 15.0) && g4.z == (int)ref_rne_quot(2.0f, g4.s), "asym zero point");
     n += 6;
   }
+  // asymmetric scales from random ranges, against the exact ceiling of (hi - lo) / 15
+  for (int i = 0; i < 300000; ++i) {
+    const float lo = -(float)std::exp(U(rng) * 12.0) * (i % 7 == 0 ? 0.f : 1.f);
+    const float hi = (float)std::exp(U(rng) * 12.0) * (i % 11 == 0 ? 0.f : 1.f);
+    for (int bits = 4; bits <= 8; bits += 4) {
+      const GroupQuant g = group_quant(lo, hi, true, bits);
+      const double levels = (double)((1 << bits) - 1);
+      const float want = ref_bf16_ceil(((double)hi - (double)lo) / levels);
+      EXPECT(g.s == want, "asym scale lo=%a hi=%a bits=%d: %a want %a", lo, hi, bits, g.s, want);
+      if (want > 0) {
+        const double zq = ref_rne_quot(-lo, want);
+        const double z = zq < 0 ? 0 : (zq > levels ? levels : zq);
+        EXPECT(g.z == (int)z, "asym zero point lo=%a s=%a: %d want %g", lo, want, g.z, z);
+      }
+      n += 2;
+    }
+  }
   // bf16 round-to-nearest-even of fp32
   for (int i = 0; i < 100000; ++i) {
     float x = (float)(U(rng) * std::exp(U(rng) * 20));
