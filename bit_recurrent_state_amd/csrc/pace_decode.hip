@@ -181,8 +181,42 @@ void decode_kernel(DecodeParams p) {
   const float a_row = p.a[(size_t)b * p.Hv + min(lane, p.Hv - 1)];
   const float b_row = p.beta[(size_t)b * p.Hv + min(lane, p.Hv - 1)];
 
-  // state codes of this lane: strip st = wave + kWaves * s, column st*16 + l16, keys of
-  // quarter qq (units qq*KB .. qq*KB + KB - 1)
+  // Buffered tokens: every slot of the period is loaded (fixed-trip vector loads, indices
+  // clamped to the buffer), so the addresses do not wait for the count; the slots at and
+  // past the count are loaded but never used.  They are issued before the state codes so
+  // that they land first: the projections then run strip by strip as the codes arrive.
+  const size_t kslot0 = ((size_t)b * p.Hk + kh) * p.dP;
+  const size_t vslot0 = ((size_t)b * p.Hv + h) * p.dP;
+  float* ks_buf = (float*)(p.buffer + p.off_ks);
+  float* a_buf = (float*)(p.buffer + p.off_a);
+  float* beta_buf = (float*)(p.buffer + p.off_beta);
+  constexpr int RV = D / 16;                  // 16-byte vectors per int8 code row
+  constexpr int KV4 = D / 32;                 // 16-byte vectors per 4-bit key row
+  constexpr int KIT = BUF == PACE_BUF_INT8 ? (TOK * RV + kThreads - 1) / kThreads
+                                           : (TOK * KV4 + kThreads - 1) / kThreads;
+  constexpr int VIT = BUF == PACE_BUF_INT8 ? KIT : (TOK * (D / 8) + kThreads - 1) / kThreads;
+  const int kall = BUF == PACE_BUF_INT8 ? p.dP * RV : p.dP * KV4;
+  const int vall = BUF == PACE_BUF_INT8 ? p.dP * RV : p.dP * (D / 8);
+  const uint4* kc_buf = (const uint4*)(p.buffer + p.off_kc + kslot0 * (BUF == PACE_BUF_INT8 ? D : D / 2));
+  const uint4* v_buf = (const uint4*)(p.buffer + p.off_v + vslot0 * (BUF == PACE_BUF_INT8 ? D : 2 * D));
+  uint4 kv[KIT], vv[VIT];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) kv[it] = kc_buf[min(tid + it * kThreads, kall - 1)];
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) vv[it] = v_buf[min(tid + it * kThreads, vall - 1)];
+  const int si = min(tid, p.dP - 1);
+  const float ks_l = ks_buf[kslot0 + si], a_l = a_buf[vslot0 + si], b_l = beta_buf[vslot0 + si];
+  const float vs_l = BUF == PACE_BUF_INT8 ? ((const float*)(p.buffer + p.off_vs))[vslot0 + si] : 0.f;
+
+  // scales and zero points of the whole tile (symmetric states read the scales twice
+  // instead of a zero-point region they do not have)
+  const int sc_vec = D * NG * 2 / 16;
+  const int zp_vec = asym ? D * NG * bits / 8 / 16 : 1;
+  const uint4 sc_reg = ((const uint4*)g_scales)[min(tid, sc_vec - 1)];
+  const uint4 zp_reg = ((const uint4*)(asym ? (const uint8_t*)g_zeros : (const uint8_t*)g_scales))[min(tid, zp_vec - 1)];
+
+  // state codes of this lane, strip by strip: strip st = wave + kWaves * s, column
+  // st*16 + l16, keys of quarter qq (units qq*KB .. qq*KB + KB - 1)
   constexpr int AW = HB == 4 ? KB : 2 * KB;   // code dwords per strip and lane
   uint32_t araw[SPW][AW];
 #pragma unroll
@@ -205,45 +239,14 @@ void decode_kernel(DecodeParams p) {
       }
     }
   }
-  // scales and zero points of the whole tile (symmetric states read the scales twice
-  // instead of a zero-point region they do not have)
-  const int sc_vec = D * NG * 2 / 16;
-  const int zp_vec = asym ? D * NG * bits / 8 / 16 : 1;
-  const uint4 sc_reg = ((const uint4*)g_scales)[min(tid, sc_vec - 1)];
-  const uint4 zp_reg = ((const uint4*)(asym ? (const uint8_t*)g_zeros : (const uint8_t*)g_scales))[min(tid, zp_vec - 1)];
-
-  // the state stream is in flight before the first use of the count
-  __builtin_amdgcn_sched_barrier(0);
 
   // counts outside [0, dP) cannot come from this library; clamp so that every slot
   // index stays inside the buffer whatever the buffer holds
   const int n0 = min(max(count_raw, 0), p.dP - 1);
   const int n = flush_only ? n0 : n0 + 1;
   const bool do_flush = flush_only || n >= p.dP;
-
-  // buffered tokens 0..n0-1: fixed-trip vector loads with clamped indices
-  const size_t kslot0 = ((size_t)b * p.Hk + kh) * p.dP;
-  const size_t vslot0 = ((size_t)b * p.Hv + h) * p.dP;
-  float* ks_buf = (float*)(p.buffer + p.off_ks);
-  float* a_buf = (float*)(p.buffer + p.off_a);
-  float* beta_buf = (float*)(p.buffer + p.off_beta);
-  constexpr int RV = D / 16;                  // 16-byte vectors per int8 code row
-  constexpr int KV4 = D / 32;                 // 16-byte vectors per 4-bit key row
-  constexpr int KIT = BUF == PACE_BUF_INT8 ? ((TOK - 1) * RV + kThreads - 1) / kThreads
-                                           : ((TOK - 1) * KV4 + kThreads - 1) / kThreads;
-  constexpr int VIT = BUF == PACE_BUF_INT8 ? KIT : ((TOK - 1) * (D / 8) + kThreads - 1) / kThreads;
   const int kvec = BUF == PACE_BUF_INT8 ? n0 * RV : n0 * KV4;
   const int vvec = BUF == PACE_BUF_INT8 ? n0 * RV : n0 * (D / 8);
-  const uint4* kc_buf = (const uint4*)(p.buffer + p.off_kc + kslot0 * (BUF == PACE_BUF_INT8 ? D : D / 2));
-  const uint4* v_buf = (const uint4*)(p.buffer + p.off_v + vslot0 * (BUF == PACE_BUF_INT8 ? D : 2 * D));
-  uint4 kv[KIT], vv[VIT];
-#pragma unroll
-  for (int it = 0; it < KIT; ++it) kv[it] = kc_buf[min(tid + it * kThreads, max(kvec - 1, 0))];
-#pragma unroll
-  for (int it = 0; it < VIT; ++it) vv[it] = v_buf[min(tid + it * kThreads, max(vvec - 1, 0))];
-  const int si = min(tid, max(n0 - 1, 0));
-  const float ks_l = ks_buf[kslot0 + si], a_l = a_buf[vslot0 + si], b_l = beta_buf[vslot0 + si];
-  const float vs_l = BUF == PACE_BUF_INT8 ? ((const float*)(p.buffer + p.off_vs))[vslot0 + si] : 0.f;
   // keep the scheduler from pulling the first uses of the token (and their waits)
   // above the remaining load issues
   __builtin_amdgcn_sched_barrier(0);
