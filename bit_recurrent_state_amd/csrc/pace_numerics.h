@@ -81,6 +81,28 @@ __host__ __device__ inline float bf16_ceil_div(float m, float k, float rk) {
   return bits_f32(u);
 }
 
+// Correctly rounded 1 / s for a bf16-valued s >= 2^-126 from any estimate r0 within an
+// fp32 ulp of it: the residual 1 - r0 s is exact in one fused multiply-add, and one
+// Newton step in fma form then rounds correctly for each of the 128 bf16 significands
+// (checked exhaustively with exact rationals, for every start within an ulp).
+__host__ __device__ inline float rcp_fix(float s, float r0) {
+  const float e = fmaf(-r0, s, 1.0f);
+  return fmaf(e, r0, r0);
+}
+
+// 1 / s, correctly rounded, for a bf16-valued scale 2^-126 <= s <= 2^126 (on the device:
+// the hardware reciprocal, within an ulp, and one correction).  Scales below 2^-126 (a
+// group whose values all lie under 2^-123 in magnitude) take 1 / 2^-126 instead, which
+// keeps x / s bounded by the code range, so their codes stay valid.
+__host__ __device__ inline float rcp_bf16(float s) {
+  const float c = fmaxf(s, 0x1p-126f);
+#if defined(__HIP_DEVICE_COMPILE__)
+  return rcp_fix(c, __builtin_amdgcn_rcpf(c));
+#else
+  return 1.0f / c;
+#endif
+}
+
 // round-half-to-even(x / s) for fp32 x and a bf16-valued scale s > 0, exactly.
 // r = 1/s (any fp32 approximation).  A first guess n = rne(x * r) is within one of the
 // answer; the residual e = x - n*s is exact in fp32 (s has 8 significant bits and
@@ -109,7 +131,7 @@ __host__ __device__ inline float rne_quotient(float x, float s, float r) {
 // lo = min(0, min), hi = max(0, max), s = bf16_ceil((hi - lo) / (2^b - 1)),
 // z = clip(rne(-lo / s), 0, 2^b - 1) decided exactly.  s = 0 gives z = 0 (asym).
 struct GroupQuant {
-  float s, r;   // scale and its reciprocal (0 when s = 0)
+  float s, r;   // scale and its correctly rounded reciprocal (0 when s = 0)
   int z;        // zero point / stored offset
 };
 
@@ -130,9 +152,9 @@ __host__ __device__ inline GroupQuant group_quant(float mn, float mx, bool asym,
     float range = a + b;
     if (b - (range - a) > 0.f) range = bits_f32(f32_bits(range) + 1u);
     q.s = bf16_ceil_div(range, (float)levels, bits == 8 ? 1.0f / 255.0f : 1.0f / 15.0f);
-    q.z = q.s > 0.f ? (int)fminf(fmaxf(rne_quotient(-lo, q.s, 1.0f / q.s), 0.f), (float)levels) : 0;
   }
-  q.r = q.s > 0.f ? 1.0f / q.s : 0.f;
+  q.r = q.s > 0.f ? rcp_bf16(q.s) : 0.f;
+  if (asym) q.z = q.s > 0.f ? (int)fminf(fmaxf(rne_quotient(-fminf(mn, 0.f), q.s, q.r), 0.f), (float)levels) : 0;
   return q;
 }
 

@@ -70,6 +70,21 @@ int main() {
     EXPECT(got == want, "div_rn(%a, %g) = %a want %a", m, k, got, want);
     n++;
   }
+  // reciprocal correction: every normal bf16 value, from each start within an ulp of the
+  // correctly rounded reciprocal, lands on it (host rcp_bf16 is the IEEE division)
+  for (uint32_t b = 0x0080u; b < 0x7F80u; ++b) {
+    const float s = bf16_to_f32((uint16_t)b);
+    volatile float vs = s;
+    const float want = 1.0f / vs;
+    if (!std::isfinite(want) || want < 0x1p-126f) continue;
+    const float starts[3] = {std::nextafter(want, 0.f), want, std::nextafter(want, INFINITY)};
+    for (float r0 : starts) {
+      const float got = rcp_fix(s, r0);
+      EXPECT(got == want, "rcp_fix(%a, %a) = %a want %a", s, r0, got, want);
+      n++;
+    }
+    EXPECT(rcp_bf16(s) == want, "rcp_bf16(%a)", s);
+  }
   // exact RNE quotient, including constructed exact ties and near ties
   for (int i = 0; i < 400000; ++i) {
     float s = ref_bf16_ceil(std::exp(U(rng) * 10.0));
