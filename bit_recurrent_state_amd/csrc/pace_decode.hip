@@ -9,9 +9,10 @@
 // One workgroup of 2 waves owns one (sequence, value head) tile, so all B x Hv tiles of
 // a layer are resident at once (8 workgroups per CU).  With S_0 the dequantised state,
 // k^_i / v^_i the buffered (quantised) tokens and q the query:
-//   prologue     every load that does not depend on the buffer count (state codes into
-//                registers, scales / zero points, the current token) is issued before
-//                anything waits; the buffered tokens follow the count.
+//   prologue     the current token, its gates, every buffer slot of the period and the
+//                tile's scales / zero points are requested at once (no address waits
+//                for the count); the state codes (into registers) follow as soon as the
+//                token is here, so token work overlaps the state stream.
 //   projections  p_i = S_0^T k^_i and r = S_0^T q on the int8 matrix cores: stored codes
 //                (A) times the buffer's key codes and three exact int8 pieces of q (B),
 //                one 32-key block per MFMA so every MFMA lies inside one scale group;
@@ -183,8 +184,7 @@ void decode_kernel(DecodeParams p) {
 
   // Buffered tokens: every slot of the period is loaded (fixed-trip vector loads, indices
   // clamped to the buffer), so the addresses do not wait for the count; the slots at and
-  // past the count are loaded but never used.  They are issued before the state codes so
-  // that they land first: the projections then run strip by strip as the codes arrive.
+  // past the count are loaded but never used.
   const size_t kslot0 = ((size_t)b * p.Hk + kh) * p.dP;
   const size_t vslot0 = ((size_t)b * p.Hv + h) * p.dP;
   float* ks_buf = (float*)(p.buffer + p.off_ks);
@@ -215,31 +215,6 @@ void decode_kernel(DecodeParams p) {
   const uint4 sc_reg = ((const uint4*)g_scales)[min(tid, sc_vec - 1)];
   const uint4 zp_reg = ((const uint4*)(asym ? (const uint8_t*)g_zeros : (const uint8_t*)g_scales))[min(tid, zp_vec - 1)];
 
-  // state codes of this lane, strip by strip: strip st = wave + kWaves * s, column
-  // st*16 + l16, keys of quarter qq (units qq*KB .. qq*KB + KB - 1)
-  constexpr int AW = HB == 4 ? KB : 2 * KB;   // code dwords per strip and lane
-  uint32_t araw[SPW][AW];
-#pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    const int c = (wave + kWaves * s) * 16 + l16;
-    const uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
-    if (!is8) {
-      if constexpr (KB == 4) {
-        const uint4 v = *(const uint4*)colp;
-        araw[s][0] = v.x; araw[s][1] = v.y; araw[s][2] = v.z; araw[s][3] = v.w;
-      } else {
-        const uint2 v = *(const uint2*)colp;
-        araw[s][0] = v.x; araw[s][1] = v.y;
-      }
-    } else if constexpr (HB != 4) {
-#pragma unroll
-      for (int kb = 0; kb < KB; kb += 2) {
-        const uint4 v = *(const uint4*)(colp + kb * 8);
-        araw[s][2 * kb] = v.x; araw[s][2 * kb + 1] = v.y; araw[s][2 * kb + 2] = v.z; araw[s][2 * kb + 3] = v.w;
-      }
-    }
-  }
-
   // counts outside [0, dP) cannot come from this library; clamp so that every slot
   // index stays inside the buffer whatever the buffer holds
   const int n0 = min(max(count_raw, 0), p.dP - 1);
@@ -265,6 +240,33 @@ void decode_kernel(DecodeParams p) {
   // exit before it would hold every load back until the flag and the count have arrived.
   // Both are uniform over the workgroup, so the whole tile leaves together.
   if (!active || (flush_only && count_raw <= 0)) return;   // (nothing buffered: nothing to flush)
+  // State codes of this lane, strip by strip: strip st = wave + kWaves * s, column
+  // st*16 + l16, keys of quarter qq (units qq*KB .. qq*KB + KB - 1).  Requested only once
+  // the current token is here: the token-sized loads of every tile are then served ahead
+  // of the state stream, so the work that needs only tokens runs while the codes arrive.
+  constexpr int AW = HB == 4 ? KB : 2 * KB;   // code dwords per strip and lane
+  uint32_t araw[SPW][AW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int c = (wave + kWaves * s) * 16 + l16;
+    const uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
+    if (!is8) {
+      if constexpr (KB == 4) {
+        const uint4 v = *(const uint4*)colp;
+        araw[s][0] = v.x; araw[s][1] = v.y; araw[s][2] = v.z; araw[s][3] = v.w;
+      } else {
+        const uint2 v = *(const uint2*)colp;
+        araw[s][0] = v.x; araw[s][1] = v.y;
+      }
+    } else if constexpr (HB != 4) {
+#pragma unroll
+      for (int kb = 0; kb < KB; kb += 2) {
+        const uint4 v = *(const uint4*)(colp + kb * 8);
+        araw[s][2 * kb] = v.x; araw[s][2 * kb + 1] = v.y; araw[s][2 * kb + 2] = v.z; araw[s][2 * kb + 3] = v.w;
+      }
+    }
+  }
+
   if (!flush_only) {
     float Mk = sm.red[0][0], Mv = sm.red[1][0], Mq = sm.red[2][0];
 #pragma unroll
