@@ -11,8 +11,9 @@
 // k^_i / v^_i the buffered (quantised) tokens and q the query:
 //   prologue     the current token, its gates, every buffer slot of the period and the
 //                tile's scales / zero points are requested at once (no address waits
-//                for the count); the state codes (into registers) follow as soon as the
-//                token is here, so token work overlaps the state stream.
+//                for the count); the state codes (into registers) are requested once
+//                the token phase has used them, so the whole launch's token traffic is
+//                served ahead of the state stream.
 //   projections  p_i = S_0^T k^_i and r = S_0^T q on the int8 matrix cores: stored codes
 //                (A) times the buffer's key codes and three exact int8 pieces of q (B),
 //                one 32-key block per MFMA so every MFMA lies inside one scale group;
@@ -240,33 +241,6 @@ void decode_kernel(DecodeParams p) {
   // exit before it would hold every load back until the flag and the count have arrived.
   // Both are uniform over the workgroup, so the whole tile leaves together.
   if (!active || (flush_only && count_raw <= 0)) return;   // (nothing buffered: nothing to flush)
-  // State codes of this lane, strip by strip: strip st = wave + kWaves * s, column
-  // st*16 + l16, keys of quarter qq (units qq*KB .. qq*KB + KB - 1).  Requested only once
-  // the current token is here: the token-sized loads of every tile are then served ahead
-  // of the state stream, so the work that needs only tokens runs while the codes arrive.
-  constexpr int AW = HB == 4 ? KB : 2 * KB;   // code dwords per strip and lane
-  uint32_t araw[SPW][AW];
-#pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    const int c = (wave + kWaves * s) * 16 + l16;
-    const uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
-    if (!is8) {
-      if constexpr (KB == 4) {
-        const uint4 v = *(const uint4*)colp;
-        araw[s][0] = v.x; araw[s][1] = v.y; araw[s][2] = v.z; araw[s][3] = v.w;
-      } else {
-        const uint2 v = *(const uint2*)colp;
-        araw[s][0] = v.x; araw[s][1] = v.y;
-      }
-    } else if constexpr (HB != 4) {
-#pragma unroll
-      for (int kb = 0; kb < KB; kb += 2) {
-        const uint4 v = *(const uint4*)(colp + kb * 8);
-        araw[s][2 * kb] = v.x; araw[s][2 * kb + 1] = v.y; araw[s][2 * kb + 2] = v.z; araw[s][2 * kb + 3] = v.w;
-      }
-    }
-  }
-
   if (!flush_only) {
     float Mk = sm.red[0][0], Mv = sm.red[1][0], Mq = sm.red[2][0];
 #pragma unroll
@@ -413,6 +387,34 @@ void decode_kernel(DecodeParams p) {
       }
     }
   }
+  // State codes of this lane, strip by strip: strip st = wave + kWaves * s, column
+  // st*16 + l16, keys of quarter qq (units qq*KB .. qq*KB + KB - 1).  Requested only now,
+  // with the token phase done: the token-sized loads of every tile (current token,
+  // buffer, scales) are then served ahead of the state stream, and each tile meets its
+  // codes with nothing left to do but the projections.
+  constexpr int AW = HB == 4 ? KB : 2 * KB;   // code dwords per strip and lane
+  uint32_t araw[SPW][AW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int c = (wave + kWaves * s) * 16 + l16;
+    const uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
+    if (!is8) {
+      if constexpr (KB == 4) {
+        const uint4 v = *(const uint4*)colp;
+        araw[s][0] = v.x; araw[s][1] = v.y; araw[s][2] = v.z; araw[s][3] = v.w;
+      } else {
+        const uint2 v = *(const uint2*)colp;
+        araw[s][0] = v.x; araw[s][1] = v.y;
+      }
+    } else if constexpr (HB != 4) {
+#pragma unroll
+      for (int kb = 0; kb < KB; kb += 2) {
+        const uint4 v = *(const uint4*)(colp + kb * 8);
+        araw[s][2 * kb] = v.x; araw[s][2 * kb + 1] = v.y; araw[s][2 * kb + 2] = v.z; araw[s][2 * kb + 3] = v.w;
+      }
+    }
+  }
+
   __syncthreads();
   if (BUF == PACE_BUF_K4_VBF16 && !flush_only && !do_flush && (h % p.gamma) == 0 && tid < D / 2) {
     const int m = tid / 4, w = tid % 4;
