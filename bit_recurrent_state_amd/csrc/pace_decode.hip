@@ -143,7 +143,17 @@ void decode_kernel(DecodeParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, qq = lane >> 4;
-  const int h = blockIdx.x, b = blockIdx.y;
+  // The value heads of one key head run on one XCD, so that the key token, the query and
+  // the buffered keys they share are fetched into one L2: workgroups are dealt to the 8
+  // XCDs in turn by linear id, so within each block of 8 gamma heads the heads of one key
+  // head are placed 8 ids apart (power-of-two gamma, Hv a multiple of 8 gamma).
+  int h = blockIdx.x;
+  const int b = blockIdx.y;
+  if (p.gamma > 1 && (p.gamma & (p.gamma - 1)) == 0 && p.Hv % (8 * p.gamma) == 0) {
+    const int lg = __builtin_ctz(p.gamma);
+    const int r = h & (8 * p.gamma - 1);
+    h = ((((h >> (3 + lg)) << 3) + (r & 7)) << lg) | (r >> 3);
+  }
   const int kh = h / p.gamma;
 
   // ---------------------------------------------------------------- prologue
@@ -627,6 +637,7 @@ void decode_kernel(DecodeParams p) {
   // ----------------------------------------- flush: fold on MFMA, requantise
   const float gn = sm.gamma_n;
   const int ax16 = (lane ^ 16) << 2, ax32 = (lane ^ 32) << 2;   // lanes of the other quarters
+  const int qaddr = l16 << 2;                                       // lane (0, l16); + 64 g: (g, l16)
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     const int c = (wave + kWaves * s) * 16 + l16;    // this lane's column
@@ -671,16 +682,20 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int t = 0; t < 2 * KB; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[t], bw, acc[t], 0, 0, 0);
     }
-    // requantise each (column, group) and write back in place
-    uint32_t outw[AW];
-#pragma unroll
-    for (int i = 0; i < AW; ++i) outw[i] = 0;
-    int zprev = 0;
+    // Requantise each (column, group) and write back in place.  Every group's range is
+    // reduced over the four lanes (quarters) of the column; then each lane derives the
+    // quantiser of one group (qq mod NG) and the others read it, rather than all four
+    // lanes deriving every group.
+    float gmx[4], gmn[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+      gmx[g] = 0.f;
+      gmn[g] = 0.f;
       if (g >= NG) break;
-      float mx = -INFINITY, mn = INFINITY;
+      float mx, mn;
       if (asym) {
+        mx = -INFINITY;
+        mn = INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           if (kb / kpg != g) continue;
@@ -703,8 +718,48 @@ void decode_kernel(DecodeParams p) {
         mx = fmaxf(mx, lane_read(ax16, mx)); mx = fmaxf(mx, lane_read(ax32, mx));
         mn = -mx;
       }
-      const GroupQuant gq = group_quant(mn, mx, asym, bits);
-      const CodeRange cr = code_range(gq.z, asym, bits);
+      gmx[g] = mx;
+      gmn[g] = mn;
+    }
+    const int gm = qq & (NG - 1);           // this lane's group (NG is 1, 2 or 4)
+    float mxm = gmx[0], mnm = gmn[0];
+#pragma unroll
+    for (int g = 1; g < 4; ++g) {
+      mxm = g == gm ? gmx[g] : mxm;
+      mnm = g == gm ? gmn[g] : mnm;
+    }
+    const GroupQuant gq = group_quant(mnm, mxm, asym, bits);
+    float rg[4];
+    int zg[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {           // the quantiser of group g from lane (g, l16)
+      rg[g] = 0.f;
+      zg[g] = 0;
+      if (g >= NG) break;
+      rg[g] = lane_read(qaddr + 64 * g, gq.r);
+      if (asym) zg[g] = __builtin_amdgcn_ds_bpermute(qaddr + 64 * g, gq.z);
+    }
+    if (qq < NG) {
+      g_scales[c * NG + qq] = (uint16_t)(f32_bits(gq.s) >> 16);
+      if (asym) {
+        const int e = c * NG + qq;
+        if (is8) {
+          g_zeros[e] = (uint8_t)gq.z;
+        } else if (e & 1) {                 // two 4-bit zero points a byte, low nibble first
+          int zlo = zg[0];
+#pragma unroll
+          for (int g = 1; g < 4; ++g) zlo = g == qq - 1 ? zg[g] : zlo;
+          g_zeros[e >> 1] = (uint8_t)(zlo | (gq.z << 4));
+        }
+      }
+    }
+    uint32_t outw[AW];
+#pragma unroll
+    for (int i = 0; i < AW; ++i) outw[i] = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (g >= NG) break;
+      const CodeRange cr = code_range(asym ? zg[g] : 1 << (bits - 1), asym, bits);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         if (kb / kpg != g) continue;
@@ -714,7 +769,7 @@ void decode_kernel(DecodeParams p) {
         uint32_t f0[4], f1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float y0 = fmaf(acc[2 * kb][i], gq.r, cr.magic), y1 = fmaf(acc[2 * kb + 1][i], gq.r, cr.magic);
+          float y0 = fmaf(acc[2 * kb][i], rg[g], cr.magic), y1 = fmaf(acc[2 * kb + 1][i], rg[g], cr.magic);
           if (asym) {
             y0 = fminf(fmaxf(y0, cr.lo), cr.hi);
             y1 = fminf(fmaxf(y1, cr.lo), cr.hi);
@@ -731,15 +786,6 @@ void decode_kernel(DecodeParams p) {
           outw[2 * kb + 1] = hi;
         }
       }
-      if (qq == 0) {
-        g_scales[c * NG + g] = (uint16_t)(f32_bits(gq.s) >> 16);
-        if (asym) {
-          const int e = c * NG + g;
-          if (is8) g_zeros[e] = (uint8_t)gq.z;
-          else if (e & 1) g_zeros[e >> 1] = (uint8_t)(zprev | (gq.z << 4));
-        }
-      }
-      zprev = gq.z;
     }
     uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
     if (!is8) {
