@@ -193,9 +193,11 @@ void decode_kernel(DecodeParams p) {
   const float a_row = p.a[(size_t)b * p.Hv + min(lane, p.Hv - 1)];
   const float b_row = p.beta[(size_t)b * p.Hv + min(lane, p.Hv - 1)];
 
-  // Buffered tokens: every slot of the period is loaded (fixed-trip vector loads, indices
-  // clamped to the buffer), so the addresses do not wait for the count; the slots at and
-  // past the count are loaded but never used.
+  // Buffered tokens.  The slots of the first half of the period are requested at once
+  // (fixed-trip vector loads, indices clamped to that half), so their addresses do not
+  // wait for the count; those of the second half only when the count has reached them,
+  // as soon as it is known.  Slots at and past the count are loaded only in the first
+  // half, and never used.
   const size_t kslot0 = ((size_t)b * p.Hk + kh) * p.dP;
   const size_t vslot0 = ((size_t)b * p.Hv + h) * p.dP;
   float* ks_buf = (float*)(p.buffer + p.off_ks);
@@ -206,15 +208,16 @@ void decode_kernel(DecodeParams p) {
   constexpr int KIT = BUF == PACE_BUF_INT8 ? (TOK * RV + kThreads - 1) / kThreads
                                            : (TOK * KV4 + kThreads - 1) / kThreads;
   constexpr int VIT = BUF == PACE_BUF_INT8 ? KIT : (TOK * (D / 8) + kThreads - 1) / kThreads;
-  const int kall = BUF == PACE_BUF_INT8 ? p.dP * RV : p.dP * KV4;
-  const int vall = BUF == PACE_BUF_INT8 ? p.dP * RV : p.dP * (D / 8);
+  constexpr int VK = BUF == PACE_BUF_INT8 ? RV : KV4;        // key vectors per slot
+  constexpr int VV = BUF == PACE_BUF_INT8 ? RV : D / 8;      // value vectors per slot
+  const int early = min(TOK / 2, p.dP);                      // slots requested at once
   const uint4* kc_buf = (const uint4*)(p.buffer + p.off_kc + kslot0 * (BUF == PACE_BUF_INT8 ? D : D / 2));
   const uint4* v_buf = (const uint4*)(p.buffer + p.off_v + vslot0 * (BUF == PACE_BUF_INT8 ? D : 2 * D));
   uint4 kv[KIT], vv[VIT];
 #pragma unroll
-  for (int it = 0; it < KIT; ++it) kv[it] = kc_buf[min(tid + it * kThreads, kall - 1)];
+  for (int it = 0; it < KIT; ++it) kv[it] = kc_buf[min(tid + it * kThreads, early * VK - 1)];
 #pragma unroll
-  for (int it = 0; it < VIT; ++it) vv[it] = v_buf[min(tid + it * kThreads, vall - 1)];
+  for (int it = 0; it < VIT; ++it) vv[it] = v_buf[min(tid + it * kThreads, early * VV - 1)];
   const int si = min(tid, p.dP - 1);
   const float ks_l = ks_buf[kslot0 + si], a_l = a_buf[vslot0 + si], b_l = beta_buf[vslot0 + si];
   const float vs_l = BUF == PACE_BUF_INT8 ? ((const float*)(p.buffer + p.off_vs))[vslot0 + si] : 0.f;
@@ -231,8 +234,20 @@ void decode_kernel(DecodeParams p) {
   const int n0 = min(max(count_raw, 0), p.dP - 1);
   const int n = flush_only ? n0 : n0 + 1;
   const bool do_flush = flush_only || n >= p.dP;
-  const int kvec = BUF == PACE_BUF_INT8 ? n0 * RV : n0 * KV4;
-  const int vvec = BUF == PACE_BUF_INT8 ? n0 * RV : n0 * (D / 8);
+  const int kvec = n0 * VK, vvec = n0 * VV;
+  uint4 kvl[KIT], vvl[VIT];                   // second half of the period, slots < n0
+  if (n0 > early) {
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int i = tid + it * kThreads;
+      if (i >= early * VK && i < kvec) kvl[it] = kc_buf[i];
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int i = tid + it * kThreads;
+      if (i >= early * VV && i < vvec) vvl[it] = v_buf[i];
+    }
+  }
   // keep the scheduler from pulling the first uses of the token (and their waits)
   // above the remaining load issues
   __builtin_amdgcn_sched_barrier(0);
@@ -318,23 +333,17 @@ void decode_kernel(DecodeParams p) {
   }
 
   // ---------------------------------------------------------------- LDS fills
-  if (BUF == PACE_BUF_INT8) {
+  // buffered slots [s0, s1) into LDS, from the first-half or the second-half registers
+  auto fill_slots = [&](int s0, int s1, const uint4* kv, const uint4* vv) {
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int i = tid + it * kThreads;
-      if (i < kvec) {
+      if (i < s0 * VK || i >= s1 * VK) continue;
+      if (BUF == PACE_BUF_INT8) {
         *(uint4*)&sm.kc[i / RV][16 * (i % RV)] = kv[it];
-        ((uint4*)&sm.v.c[0][0])[i] = vv[it];
-      }
-    }
-    if (tid < n0) sm.vs[tid] = vs_l;
-  } else {
-    // 4-bit keys: 16 bytes = four 8-key units; byte w of unit m holds keys 8m+w (low
-    // nibble) and 8m+4+w (high nibble), each stored as c + 8.
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int i = tid + it * kThreads;
-      if (i < kvec) {
+      } else {
+        // 4-bit keys: 16 bytes = four 8-key units; byte w of unit m holds keys 8m+w (low
+        // nibble) and 8m+4+w (high nibble), each stored as c + 8.
         const uint32_t w4[4] = {kv[it].x, kv[it].y, kv[it].z, kv[it].w};
         uint32_t out[8];
 #pragma unroll
@@ -352,9 +361,13 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
       const int i = tid + it * kThreads;
-      if (i < vvec) ((uint4*)&sm.v.b[0][0])[i] = vv[it];
+      if (i < s0 * VV || i >= s1 * VV) continue;
+      if (BUF == PACE_BUF_INT8) ((uint4*)&sm.v.c[0][0])[i] = vv[it];
+      else ((uint4*)&sm.v.b[0][0])[i] = vv[it];
     }
-  }
+  };
+  fill_slots(0, min(n0, early), kv, vv);
+  if (BUF == PACE_BUF_INT8 && tid < n0) sm.vs[tid] = vs_l;
   if (tid < n0) {
     sm.vscale[tid] = ks_l;
     sm.ga[tid] = a_l;
@@ -424,6 +437,8 @@ void decode_kernel(DecodeParams p) {
       }
     }
   }
+
+  if (n0 > early) fill_slots(early, n0, kvl, vvl);     // (loads issued before the state's)
 
   __syncthreads();
   if (BUF == PACE_BUF_K4_VBF16 && !flush_only && !do_flush && (h % p.gamma) == 0 && tid < D / 2) {
