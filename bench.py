@@ -294,7 +294,11 @@ def prefill_flops(T, Hv, B, d, bf16_io=True, chunk=256, sb=64):
     64-token sub-block kernel issues per workgroup and sub-block, by MFMA type -- with bf16
     inputs, bf16 16x16x32 MFMAs for K K^T and Q K^T (one pass) and for K S, Q S and the
     state update (three passes each: the fp32 operand as three bf16 pieces), and fp32
-    16x16x4 MFMAs for the blocked solve and P U; with fp32 inputs, all fp32 16x16x4."""
+    16x16x4 MFMAs for the blocked solve and P U; with fp32 inputs, all fp32 16x16x4.
+    When twice the pairs fit the CUs (256 on MI355X) at d >= 128, the library splits each
+    pair over two column-block workgroups, which both issue the key-side products
+    (K K^T, Q K^T)."""
+    cs = 2 if (d >= 128 and 2 * B * Hv <= 256) else 1
     C = chunk
     per_chunk = 2 * (2.5 * C * C * d + 3 * C * d * d + C ** 3 / 6)
     alg = per_chunk * (-(-T // C)) * B * Hv
@@ -303,11 +307,11 @@ def prefill_flops(T, Hv, B, d, bf16_io=True, chunk=256, sb=64):
     solve_f32 = (sum(4 * ib for ib in range(tt)) + 4 * tt) * ct
     pu_f32 = pairs * 4 * ct
     if bf16_io:
-        bf16 = 2 * pairs * (d // 32) + 2 * 3 * (kt // 2) * tt * ct + 3 * (tt // 2) * kt * ct
+        bf16 = cs * 2 * pairs * (d // 32) + 2 * 3 * (kt // 2) * tt * ct + 3 * (tt // 2) * kt * ct
         f32 = solve_f32 + pu_f32
     else:
         bf16 = 0
-        f32 = 2 * pairs * (d // 4) + 2 * tt * kt * 4 * ct + solve_f32 + pu_f32 + tt * 4 * kt * ct
+        f32 = cs * 2 * pairs * (d // 4) + 2 * tt * kt * 4 * ct + solve_f32 + pu_f32 + tt * 4 * kt * ct
     n = -(-T // sb) * B * Hv
     return alg, {"bf16": bf16 * 2 * 16 * 16 * 32 * n, "f32": f32 * 2 * 16 * 16 * 4 * n}
 

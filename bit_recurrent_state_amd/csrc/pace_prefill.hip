@@ -21,8 +21,13 @@
 // bf16 pieces (v_mfma_f32_16x16x32_bf16), and the small P U and solve products use
 // v_mfma_f32_16x16x4_f32; with fp32 inputs everything uses the fp32 MFMA.
 //
-// One workgroup (4 wave64s) per (sequence, value head).  The state S lives in the MFMA
-// accumulators for the whole call: wave w owns value columns [w D/4, (w+1) D/4), all keys;
+// One workgroup (4 wave64s) per (sequence, value head) and block of D/CS value columns:
+// the recurrence is independent per value column (keys and gates are shared, the
+// rounding groups run along the keys of one column), so when twice the (sequence, head)
+// pairs still fit the CUs in one round, CS = 2 splits each one over two workgroups that
+// repeat only the key-side work (Gram, query-key tiles, the triangular solve).  The
+// state S lives in the MFMA accumulators for the whole call: wave w owns its block's
+// value columns [w DC/4, (w+1) DC/4) (DC = D/CS), all keys;
 // lane l of a 16x16 accumulator tile holds rows 4(l/16)+r, column l%16.  Contractions over
 // keys use those accumulators directly as the B operand, pairing them with an A operand
 // read in the matching (permuted) key order.  The next sub-block's inputs are prefetched
@@ -235,10 +240,11 @@ struct Smem {
   float wend[kSB];                     // e^{g_end - g_t}
 };
 
-template <int D, int IO>
+template <int D, int IO, int CS>
 __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
   constexpr int KT = D / 16;           // key tiles
-  constexpr int CT = D / 64;           // column tiles per wave
+  constexpr int CT = D / (64 * CS);    // column tiles per wave
+  static_assert(CT >= 1, "a wave owns at least one 16-column tile");
   constexpr int TT = kSB / 16;         // token tiles
   constexpr int VS = IO == 1 ? 8 : 4;  // elements per 16-byte input vector
   using I = Inputs<D, IO>;
@@ -246,7 +252,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, qd = lane >> 4;
-  const int b = blockIdx.x / p.Hv, h = blockIdx.x % p.Hv, kh = h / p.gamma;
+  const int tile = blockIdx.x / CS, cb = (blockIdx.x % CS) * (D / CS);   // first column
+  const int b = tile / p.Hv, h = tile % p.Hv, kh = h / p.gamma;
 
   const bool is8 = (p.mask8 >> h) & 1ull;
   const uint64_t below = h ? (p.mask8 & ((1ull << h) - 1ull)) : 0ull;
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
     const uint8_t* zsrc = p.asym ? rec.zeros : (const uint8_t*)rec.scales;
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-      const int j = 16 * (wave * CT + c) + l16;
+      const int j = cb + 16 * (wave * CT + c) + l16;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         const int m = 2 * kt + (qd >> 1);
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
     }
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-      const int j = 16 * (wave * CT + c) + l16;
+      const int j = cb + 16 * (wave * CT + c) + l16;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         const int e = j * rec.NG + (16 * kt) / p.group;
@@ -463,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
     v4f R[CT][TT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-      const int j = 16 * (wave * CT + c) + l16;
+      const int j = cb + 16 * (wave * CT + c) + l16;
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
       }
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        const int j = 16 * (wave * CT + c) + l16;
+        const int j = cb + 16 * (wave * CT + c) + l16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * tt + 4 * qd + r;
@@ -619,7 +626,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
     if (done % p.chunk == 0 || done == p.T) {
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        const int j = 16 * (wave * CT + c) + l16;
+        const int j = cb + 16 * (wave * CT + c) + l16;
         if (p.group == 64) requant_tile<D, 64>(S[c], rec, j, qd);
         else requant_tile<D, 32>(S[c], rec, j, qd);
       }
@@ -628,10 +635,30 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
   }
 }
 
+// Compute units of the current device (one workgroup of this kernel fills a CU's LDS).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int D, int IO>
 void launch_wy(const PrefillParams& p, hipStream_t stream) {
-  const unsigned grid = (unsigned)p.B * (unsigned)p.Hv;
-  hipLaunchKernelGGL((prefill_wy_kernel<D, IO>), dim3(grid), dim3(kThreads), 0, stream, p);
+  const unsigned tiles = (unsigned)p.B * (unsigned)p.Hv;
+  // when two workgroups per (sequence, head) still run in one round, split the columns
+  if constexpr (D >= 128) {
+    if (2 * tiles <= (unsigned)device_cus()) {
+      hipLaunchKernelGGL((prefill_wy_kernel<D, IO, 2>), dim3(2 * tiles), dim3(kThreads), 0, stream, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((prefill_wy_kernel<D, IO, 1>), dim3(tiles), dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace

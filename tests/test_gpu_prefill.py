@@ -109,6 +109,20 @@ def test_prefill_long_shape_first_chunk_sampled():
     check_prefill_call(ocfg, gcfg, zero, toks.span(0, 256), tiles, "long/first-chunk")
 
 
+def test_prefill_many_pairs_one_block_per_pair():
+    """512 (sequence, head) pairs at d = 128: one workgroup per pair owns all value columns
+    (fewer pairs split each one over two column blocks, as every test above does); a
+    partial chunk, sampled tiles against the oracle."""
+    print("[prefill parity] 512 pairs, whole-column workgroups", flush=True)
+    B, Hv, Hk, d = 16, 32, 16, 128
+    ocfg = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, asym=False, buf="int8", dP=8, bf16_io=True)
+    gcfg = _lib().LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, bf16_io=True)
+    toks = make_tokens(16, B, 96, Hv, Hk, d, d, bf16=True)
+    zero = np.zeros(pk.state_layout(ocfg)[2], dtype=np.uint8)
+    tiles = [(0, 0), (3, 9), (7, 16), (15, 31)]
+    check_prefill_call(ocfg, gcfg, zero, toks.span(0, 96), tiles, "512pairs/partial")
+
+
 def test_long_prefill_full_size():
     """The long-prefill workload at its full size (4 sequences x 32,768 tokens, 32 value /
     16 key heads, d = 128, bf16, int4 g = 64, 128 chunks) in the launch configuration the
