@@ -28,6 +28,8 @@
 // The state is read once per step and written only on flush.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "pace_internal.h"
 #include "pace_numerics.h"
 
@@ -334,17 +336,20 @@ void decode_kernel(DecodeParams p) {
 
   // ---------------------------------------------------------------- LDS fills
   // buffered slots [s0, s1) into LDS, from the first-half or the second-half registers
-  auto fill_slots = [&](int s0, int s1, const uint4* kv, const uint4* vv) {
+  // (chosen at compile time, so the register arrays are never addressed through memory)
+  auto fill_slots = [&](int s0, int s1, auto half) {
+    constexpr bool kLate = decltype(half)::value;
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int i = tid + it * kThreads;
       if (i < s0 * VK || i >= s1 * VK) continue;
       if (BUF == PACE_BUF_INT8) {
-        *(uint4*)&sm.kc[i / RV][16 * (i % RV)] = kv[it];
+        *(uint4*)&sm.kc[i / RV][16 * (i % RV)] = kLate ? kvl[it] : kv[it];
       } else {
         // 4-bit keys: 16 bytes = four 8-key units; byte w of unit m holds keys 8m+w (low
         // nibble) and 8m+4+w (high nibble), each stored as c + 8.
-        const uint32_t w4[4] = {kv[it].x, kv[it].y, kv[it].z, kv[it].w};
+        const uint4 kx4 = kLate ? kvl[it] : kv[it];
+        const uint32_t w4[4] = {kx4.x, kx4.y, kx4.z, kx4.w};
         uint32_t out[8];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -362,11 +367,12 @@ void decode_kernel(DecodeParams p) {
     for (int it = 0; it < VIT; ++it) {
       const int i = tid + it * kThreads;
       if (i < s0 * VV || i >= s1 * VV) continue;
-      if (BUF == PACE_BUF_INT8) ((uint4*)&sm.v.c[0][0])[i] = vv[it];
-      else ((uint4*)&sm.v.b[0][0])[i] = vv[it];
+      const uint4 vx4 = kLate ? vvl[it] : vv[it];
+      if (BUF == PACE_BUF_INT8) ((uint4*)&sm.v.c[0][0])[i] = vx4;
+      else ((uint4*)&sm.v.b[0][0])[i] = vx4;
     }
   };
-  fill_slots(0, min(n0, early), kv, vv);
+  fill_slots(0, min(n0, early), std::false_type{});
   if (BUF == PACE_BUF_INT8 && tid < n0) sm.vs[tid] = vs_l;
   if (tid < n0) {
     sm.vscale[tid] = ks_l;
@@ -438,7 +444,7 @@ void decode_kernel(DecodeParams p) {
     }
   }
 
-  if (n0 > early) fill_slots(early, n0, kvl, vvl);     // (loads issued before the state's)
+  if (n0 > early) fill_slots(early, n0, std::true_type{});   // (loads issued before the state's)
 
   __syncthreads();
   if (BUF == PACE_BUF_K4_VBF16 && !flush_only && !do_flush && (h % p.gamma) == 0 && tid < D / 2) {
