@@ -355,7 +355,7 @@ def run_long_prefill(torch, pace, args):
            "mfma_util_of_dtype_peak": util,
            "note": "bf16 figures count the three split passes of the fp32 operands (exact bf16 "
                    "inputs times the state / decayed U as three bf16 pieces)",
-           "workgroups": B * Hv}
+           "workgroups": B * Hv * (2 if (d >= 128 and 2 * B * Hv <= 256) else 1)}
     log(f"long prefill: {ms:.2f} ms, {res['tokens_per_s']:,.0f} tok/s, executed "
         f"bf16 {res['executed_TFLOPs']['bf16']} TFLOP/s ({util['bf16']:.3f} of peak), "
         f"f32 {res['executed_TFLOPs']['f32']} TFLOP/s ({util['f32']:.3f} of peak), "
