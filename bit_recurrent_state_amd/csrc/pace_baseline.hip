@@ -30,7 +30,8 @@ __global__ __launch_bounds__(kThreads) void bf16_decode_kernel(Bf16Params p) {
   constexpr int CPB = CPW * (kThreads / 64); // columns per workgroup per pass
   constexpr int PASSES = D / CPB;
   constexpr bool kBf16 = IO == 1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int b = blockIdx.x / p.Hv, h = blockIdx.x % p.Hv, kh = h / p.gamma;
   const int m = lane % LPC;                  // keys 8m .. 8m+7
   float kk[8], qv[8];

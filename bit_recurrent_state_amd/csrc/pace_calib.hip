@@ -65,7 +65,8 @@ __global__ __launch_bounds__(kThreads) void calib_kernel(CalibParams p) {
   constexpr int PASSES = D / CPB;
   constexpr bool kBf16 = IO == 1;
   __shared__ double red[kThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int h = blockIdx.x, kh = h / p.gamma;
   const int m = lane % LPC;                      // keys 8m .. 8m+7
   const int width = p.group / 8;

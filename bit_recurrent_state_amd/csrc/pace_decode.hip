@@ -143,7 +143,8 @@ void decode_kernel(DecodeParams p) {
   constexpr bool kBf16 = IO == 1;
   __shared__ SM sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches and addresses
   const int l16 = lane & 15, qq = lane >> 4;
   // The value heads of one key head run on one XCD, so that the key token, the query and
   // the buffered keys they share are fetched into one L2: workgroups are dealt to the 8

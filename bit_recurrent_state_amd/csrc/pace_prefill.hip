@@ -234,10 +234,10 @@ struct Smem {
   float A[kSB][LA];                    // beta_t e^{g_t-g_i} k_t.k_i, strictly lower
   float Ti[kSB / 16][16][20];          // inverses of the diagonal blocks (I + A_ii)
   float P[kSB][LA];                    // e^{g_t-g_i} q_t.k_i, lower incl. diagonal
-  float g[kSB];                        // cumulative log decay
-  float beta[kSB];
-  float gam[kSB];                      // e^{g_t}
-  float wend[kSB];                     // e^{g_end - g_t}
+  alignas(16) float g[kSB];            // cumulative log decay
+  alignas(16) float beta[kSB];
+  alignas(16) float gam[kSB];          // e^{g_t}
+  alignas(16) float wend[kSB];         // e^{g_end - g_t}
 };
 
 template <int D, int IO, int CS>
@@ -250,7 +250,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
   using I = Inputs<D, IO>;
   __shared__ Smem<D, IO> sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches and addresses
   const int l16 = lane & 15, qd = lane >> 4;
   const int tile = blockIdx.x / CS, cb = (blockIdx.x % CS) * (D / CS);   // first column
   const int b = tile / p.Hv, h = tile % p.Hv, kh = h / p.gamma;
@@ -391,16 +392,27 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
           }
         }
       }
+      // decays and betas of every job's rows and column, read as vectors and all issued
+      // before any is used (one LDS round trip instead of one per element)
+      float4 g4[JPW], b4[JPW];
+      float gi[JPW];
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj) {
+        g4[jj] = *(const float4*)&sm.g[16 * tis[jj] + 4 * qd];
+        b4[jj] = *(const float4*)&sm.beta[16 * tis[jj] + 4 * qd];
+        gi[jj] = sm.g[16 * tjs[jj] + l16];
+      }
 #pragma unroll
       for (int jj = 0; jj < JPW; ++jj) {
         const int i = 16 * tjs[jj] + l16;
-        const float gi = sm.g[i];
+        const float gt[4] = {g4[jj].x, g4[jj].y, g4[jj].z, g4[jj].w};
+        const float bt[4] = {b4[jj].x, b4[jj].y, b4[jj].z, b4[jj].w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * tis[jj] + 4 * qd + r;
-          const float dec = exp2f(fminf(sm.g[t] - gi, 0.f));
+          const float dec = exp2f(fminf(gt[r] - gi[jj], 0.f));
           if (isqs[jj]) sm.P[t][i] = t >= i ? dec * acc[jj][r] : 0.f;
-          else sm.A[t][i] = t > i ? sm.beta[t] * dec * acc[jj][r] : 0.f;
+          else sm.A[t][i] = t > i ? bt[r] * dec * acc[jj][r] : 0.f;
         }
       }
     }
@@ -468,19 +480,28 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
     }
     // right-hand sides R = diag(beta) V - diag(beta Gamma) K S
     v4f R[CT][TT];
+    float4 bet4[TT], gam4[TT];               // this lane's rows, read as vectors up front
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      bet4[tt] = *(const float4*)&sm.beta[16 * tt + 4 * qd];
+      gam4[tt] = *(const float4*)&sm.gam[16 * tt + 4 * qd];
+    }
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       const int j = cb + 16 * (wave * CT + c) + l16;
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+      for (int tt = 0; tt < TT; ++tt) {
+        const float bt[4] = {bet4[tt].x, bet4[tt].y, bet4[tt].z, bet4[tt].w};
+        const float gt[4] = {gam4[tt].x, gam4[tt].y, gam4[tt].z, gam4[tt].w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * tt + 4 * qd + r;
           float vv;
           if constexpr (IO == 1) vv = bf16_to_f32(sm.x.V[t][j]);
           else vv = sm.x.V[t][j];
-          R[c][tt][r] = sm.beta[t] * fmaf(-sm.gam[t], KS[c][tt][r], vv);
+          R[c][tt][r] = bt[r] * fmaf(-gt[r], KS[c][tt][r], vv);
         }
+      }
     }
     __syncthreads();     // A and P complete
 
@@ -547,7 +568,10 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
 #pragma unroll
       for (int c = 0; c < CT; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[c][r] = sm.gam[16 * tt + 4 * qd + r] * QS[c][tt][r];
+        for (int r = 0; r < 4; ++r) {
+          const float gr = r == 0 ? gam4[tt].x : r == 1 ? gam4[tt].y : r == 2 ? gam4[tt].z : gam4[tt].w;
+          O[c][r] = gr * QS[c][tt][r];
+        }
 #pragma unroll
       for (int ib = 0; ib <= tt; ++ib) {
         const float4 px = *(const float4*)&sm.P[tr][16 * ib + 4 * qd];
