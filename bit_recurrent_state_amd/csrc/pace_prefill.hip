@@ -410,7 +410,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * tis[jj] + 4 * qd + r;
-          const float dec = exp2f(fminf(gt[r] - gi[jj], 0.f));
+          // (the hardware exp2: decays under 2^-126 read as 0, far below any fp32 sum)
+          const float dec = __builtin_amdgcn_exp2f(fminf(gt[r] - gi[jj], 0.f));
           if (isqs[jj]) sm.P[t][i] = t >= i ? dec * acc[jj][r] : 0.f;
           else sm.A[t][i] = t > i ? bt[r] * dec * acc[jj][r] : 0.f;
         }
@@ -550,38 +551,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
     }
 
     // ----------------------------- outputs O = diag(Gamma) Q S + P U, own columns
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int tr = 16 * tt + l16;
-      v4f O[CT];
-      if constexpr (IO == 0) {
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          const float4 qx = *(const float4*)&sm.x.Q[tr][16 * kt + 4 * qd];
-          const float qv[4] = {qx.x, qx.y, qx.z, qx.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < CT; ++c) QS[c][tt] = mfma4(qv[r], S[c][kt][r], QS[c][tt]);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gr = r == 0 ? gam4[tt].x : r == 1 ? gam4[tt].y : r == 2 ? gam4[tt].z : gam4[tt].w;
-          O[c][r] = gr * QS[c][tt][r];
-        }
-#pragma unroll
-      for (int ib = 0; ib <= tt; ++ib) {
-        const float4 px = *(const float4*)&sm.P[tr][16 * ib + 4 * qd];
-        const float pv[4] = {px.x, px.y, px.z, px.w};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int c = 0; c < CT; ++c)
-            O[c] = mfma4(pv[s], U[c][ib][s], O[c]);
-      }
+    auto store_out = [&](int tt, const v4f (&O)[CT]) {
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
         const int j = cb + 16 * (wave * CT + c) + l16;
@@ -594,6 +564,69 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
             else ((float*)p.o)[oi] = O[c][r];
           }
         }
+      }
+    };
+    if constexpr (IO == 1) {
+      // all four token tiles at once, so that consecutive MFMAs feed different
+      // accumulators (the chains of P U overlap instead of running one after another)
+      v4f O[TT][CT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gr = r == 0 ? gam4[tt].x : r == 1 ? gam4[tt].y : r == 2 ? gam4[tt].z : gam4[tt].w;
+            O[tt][c][r] = gr * QS[c][tt][r];
+          }
+#pragma unroll
+      for (int ib = 0; ib < TT; ++ib) {
+        float4 px[TT];
+#pragma unroll
+        for (int tt = ib; tt < TT; ++tt) px[tt] = *(const float4*)&sm.P[16 * tt + l16][16 * ib + 4 * qd];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int tt = ib; tt < TT; ++tt) {
+            const float pv = s == 0 ? px[tt].x : s == 1 ? px[tt].y : s == 2 ? px[tt].z : px[tt].w;
+#pragma unroll
+            for (int c = 0; c < CT; ++c) O[tt][c] = mfma4(pv, U[c][ib][s], O[tt][c]);
+          }
+      }
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) store_out(tt, O[tt]);
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int tr = 16 * tt + l16;
+        v4f O[CT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const float4 qx = *(const float4*)&sm.x.Q[tr][16 * kt + 4 * qd];
+          const float qv[4] = {qx.x, qx.y, qx.z, qx.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < CT; ++c) QS[c][tt] = mfma4(qv[r], S[c][kt][r], QS[c][tt]);
+        }
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gr = r == 0 ? gam4[tt].x : r == 1 ? gam4[tt].y : r == 2 ? gam4[tt].z : gam4[tt].w;
+            O[c][r] = gr * QS[c][tt][r];
+          }
+#pragma unroll
+        for (int ib = 0; ib <= tt; ++ib) {
+          const float4 px = *(const float4*)&sm.P[tr][16 * ib + 4 * qd];
+          const float pv[4] = {px.x, px.y, px.z, px.w};
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+              O[c] = mfma4(pv[s], U[c][ib][s], O[c]);
+        }
+        store_out(tt, O);
       }
     }
 
