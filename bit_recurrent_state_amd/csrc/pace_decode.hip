@@ -17,7 +17,10 @@
 //   projections  p_i = S_0^T k^_i and r = S_0^T q on the int8 matrix cores: stored codes
 //                (A) times the buffer's key codes and three exact int8 pieces of q (B),
 //                one 32-key block per MFMA so every MFMA lies inside one scale group;
-//                scale and zero point are applied once per (column, group).
+//                asymmetric zero points enter through a second MFMA per block (A = the
+//                column's zero point in every byte), so the accumulator is the exact
+//                integer sum_k (c - z) k and one scale multiply per (column, group) is
+//                left.
 //   replay       per value column, u_i = beta_i (v^_i - a_i y_i) with
 //                y_m <- a_i y_m + (k^_i . k^_m) u_i and y_q <- a_i y_q + (k^_i . q) u_i,
 //                the buffer replay written on projections; o = y_q.
@@ -116,7 +119,7 @@ struct alignas(16) Smem {
   alignas(16) float G[NV][NV];              // Gram matrix of the slots (scaled)
   float Gq[NV];                             // k_slot . q (the q pieces combined)
   alignas(16) float scf[4][D];              // this tile's scales as fp32, [group][col]
-  alignas(16) uint8_t zeros[4][D];          // this tile's zero points, [group][col], a byte each
+  alignas(16) uint8_t zeros[D][4];          // this tile's zero points, [col][group], a byte each
   float vscale[NV];                         // key scale of each token slot / q piece scale
   float vs[TOK], ga[TOK], gb[TOK];
   float red[3][4 * kWaves];                 // row maxima of |k|, |v|, |q|
@@ -389,8 +392,9 @@ void decode_kernel(DecodeParams p) {
       *(uint4*)&sm.kc[row][16 * (i % RV)] = make_uint4(0, 0, 0, 0);
   }
   if (tid >= n && tid < NV && (tid < QS || flush_only || tid >= QS + 3)) sm.vscale[tid] = 0.f;
-  // scales and zero points regrouped [group][col]: a lane's four output columns of one
-  // group are then one vector read
+  // scales regrouped [group][col] (a lane's four output columns of one group are one
+  // vector read), zero points [col][group] (the four groups of the lane's A-operand
+  // column are one read)
   const int lng = NG == 4 ? 2 : NG - 1;      // log2 NG (NG in {1, 2, 4})
   if (tid < sc_vec) {                       // 8 bf16 scales [col][group] -> fp32
     const uint32_t w[4] = {sc_reg.x, sc_reg.y, sc_reg.z, sc_reg.w};
@@ -407,13 +411,13 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int e = 16 * tid + k;
-        sm.zeros[e & (NG - 1)][e >> lng] = (uint8_t)(w[k >> 2] >> (8 * (k & 3)));
+        sm.zeros[e >> lng][e & (NG - 1)] = (uint8_t)(w[k >> 2] >> (8 * (k & 3)));
       }
     } else {                                 // 32 packed 4-bit zero points (low nibble first)
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
         const int e = 32 * tid + k;
-        sm.zeros[e & (NG - 1)][e >> lng] = (uint8_t)((w[k >> 3] >> (4 * (k & 7))) & 15u);
+        sm.zeros[e >> lng][e & (NG - 1)] = (uint8_t)((w[k >> 3] >> (4 * (k & 7))) & 15u);
       }
     }
   }
@@ -455,25 +459,28 @@ void decode_kernel(DecodeParams p) {
   }
 
   // --------------------------------------------- B operands, group sums, Gram
-  // Zero-point term of the projections, per scale group and slot vector, on MFMA with a
-  // constant A operand (every output row holds the same value): symmetric 4-bit states
-  // store c + 8, so each group's projection carries -8 * (sum of the slot's codes over the
-  // group) and an A of -8 bytes produces exactly that term, which then seeds the group's
-  // accumulator; symmetric 8-bit codes enter the MFMA as c itself (no term); asymmetric
-  // zero points vary by column, so there the plain sums are formed (A of ones).
+  // Code-offset term of the projections, per scale group and slot vector, on MFMA with a
+  // constant A operand (every output row holds the same value), used as the seed of the
+  // group's accumulator.  Symmetric 4-bit states store c + 8, so each group's projection
+  // carries -8 * (sum of the slot's codes over the group): an A of -8 bytes produces it.
+  // Symmetric 8-bit codes and asymmetric 4-bit codes enter the MFMA as they are (no
+  // term).  Asymmetric 8-bit codes enter as c - 128 and their zero-point MFMA below adds
+  // (127 - z) times the sum, so the seed is the plain sum (A of ones).
   long bop[NT][KB];
   v4i zacc[NT][4];
-  const long zrow = asym ? 0x0101010101010101l : (is8 ? 0l : (long)0xF8F8F8F8F8F8F8F8ull);
+  const long zrow = asym ? (is8 ? 0x0101010101010101l : 0l) : (is8 ? 0l : (long)0xF8F8F8F8F8F8F8F8ull);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) bop[nt][kb] = *(const long*)&sm.kc[nt * 16 + l16][32 * kb + 8 * qq];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      zacc[nt][g] = v4i{0, 0, 0, 0};
+    for (int g = 0; g < 4; ++g) zacc[nt][g] = v4i{0, 0, 0, 0};
+    if (zrow != 0) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        if (kb / kpg == g) zacc[nt][g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(zrow, bop[nt][kb], zacc[nt][g], 0, 0, 0);
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          if (kb / kpg == g) zacc[nt][g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(zrow, bop[nt][kb], zacc[nt][g], 0, 0, 0);
     }
   }
   if (wave == kWaves - 1) {
@@ -513,9 +520,20 @@ void decode_kernel(DecodeParams p) {
       for (int i = 0; i < 4; ++i) proj[nt][i] = 0.f;
     v4i acc[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = asym ? v4i{0, 0, 0, 0} : zacc[nt][0];
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = zacc[nt][0];
+    // Asymmetric zero points: -z (4-bit) or 127 - z (8-bit, = z ^ 0x7F as a byte) of each
+    // group of the lane's A-operand column, as int8 bytes; replicated over a block's eight
+    // A bytes they add -z (resp. (127 - z)) times the slot's code sum to the row of that
+    // column, so the accumulator ends at sum_k (c - z) k exactly.
+    uint32_t zx = 0u;
+    if (asym) {
+      const uint32_t z4 = *(const uint32_t*)&sm.zeros[col0 + l16][0];
+      // per byte, 0x80 - z never borrows (z <= 15); ^ 0x80 leaves -z
+      zx = is8 ? (z4 ^ 0x7F7F7F7Fu) : ((0x80808080u - z4) ^ 0x80808080u);
+    }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      const int g = kb / kpg;
       long a;
       if (!is8) {
         const uint32_t d = araw[s][kb];
@@ -525,39 +543,26 @@ void decode_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bop[nt][kb], acc[nt], 0, 0, 0);
+      if (asym) {
+        const uint32_t zr = __builtin_amdgcn_perm(zx, zx, 0x01010101u * (uint32_t)g);   // byte g, four times
+        const long za = (long)(((unsigned long)zr << 32) | zr);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(za, bop[nt][kb], acc[nt], 0, 0, 0);
+      }
       if ((kb + 1) % kpg != 0) continue;
-      // end of scale group g: scale (and an asymmetric zero point) once per (column, group)
-      const int g = kb / kpg;
+      // end of scale group g: one scale multiply per (column, group)
       const float4 sc4 = *(const float4*)&sm.scf[g][ocol];
       const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
-      const uint32_t z4 = asym ? *(const uint32_t*)&sm.zeros[g][ocol] : 0u;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = scv[i];
-        if (asym) {
-          int z = (int)((z4 >> (8 * i)) & 0xFFu);
-          if (is8) z -= 128;              // the A operand held codes - 128
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            int ksg = 0;                    // (static selects: g may be a run-time value)
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) ksg = gg == g ? zacc[nt][gg][0] : ksg;
-            // |z| <= 255 and |ksg| <= 127 * 64: a 24-bit product
-            proj[nt][i] += (float)(acc[nt][i] - __mul24(z, ksg)) * sc;
-          }
-        } else {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) proj[nt][i] += (float)acc[nt][i] * sc;
-        }
-      }
+        for (int nt = 0; nt < NT; ++nt) proj[nt][i] += (float)acc[nt][i] * scv[i];
       if (g + 1 < NG) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           v4i nx = v4i{0, 0, 0, 0};
-          if (!asym) {
 #pragma unroll
-            for (int gg = 1; gg < 4; ++gg) nx = gg == g + 1 ? zacc[nt][gg] : nx;
-          }
+          for (int gg = 1; gg < 4; ++gg) nx = gg == g + 1 ? zacc[nt][gg] : nx;
           acc[nt] = nx;
         }
       }
@@ -669,7 +674,7 @@ void decode_kernel(DecodeParams p) {
     for (int kb = 0; kb < KB; ++kb) {
       const int g = kb / kpg;
       const float sc = sm.scf[g][c];
-      const int z = asym ? (int)sm.zeros[g][c] : 1 << (bits - 1);
+      const int z = asym ? (int)sm.zeros[c][g] : 1 << (bits - 1);
       const float gs = gn * sc, gz = -gs * (float)z;
       uint32_t b0, b1;            // 4 stored codes each (bytes): keys +0..3, +4..7
       if (!is8) {
