@@ -727,9 +727,9 @@ void decode_kernel(DecodeParams p) {
         for (int kb = 0; kb < KB; ++kb) {
           if (kb / kpg != g) continue;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            mx = fmaxf(mx, fmaxf(acc[2 * kb][i], acc[2 * kb + 1][i]));
-            mn = fminf(mn, fminf(acc[2 * kb][i], acc[2 * kb + 1][i]));
+          for (int i = 0; i < 4; ++i) {       // running chains: one max3 / min3 per two values
+            mx = fmaxf(fmaxf(mx, acc[2 * kb][i]), acc[2 * kb + 1][i]);
+            mn = fminf(fminf(mn, acc[2 * kb][i]), acc[2 * kb + 1][i]);
           }
         }
         mx = fmaxf(mx, lane_read(ax16, mx)); mx = fmaxf(mx, lane_read(ax32, mx));
@@ -740,7 +740,7 @@ void decode_kernel(DecodeParams p) {
         for (int kb = 0; kb < KB; ++kb) {
           if (kb / kpg != g) continue;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(fabsf(acc[2 * kb][i]), fabsf(acc[2 * kb + 1][i])));
+          for (int i = 0; i < 4; ++i) mx = fmaxf(fmaxf(mx, fabsf(acc[2 * kb][i])), fabsf(acc[2 * kb + 1][i]));
         }
         mx = fmaxf(mx, lane_read(ax16, mx)); mx = fmaxf(mx, lane_read(ax32, mx));
         mn = -mx;

@@ -51,6 +51,10 @@ CASES = {
     "dP16_sym_int8": (2, 4, 2, 64, 32, False, "int8", True, 16, None),
     "dP32_asym_int8": (2, 4, 2, 64, 32, True, "int8", False, 32, [4, 8, 4, 4]),
     "sym8_heads": (2, 4, 2, 128, 64, False, "int8", True, 8, [8, 8, 4, 8]),
+    # asymmetric 64-key groups (two 32-key MFMA blocks per group); symmetric state with the
+    # mixed buffer
+    "asym_g64_int8": (2, 8, 4, 128, 64, True, "int8", True, 8, [4, 8, 4, 4, 8, 4, 4, 4]),
+    "sym4_g64_mixed": (2, 8, 4, 128, 64, False, "mixed", True, 8, None),
 }
 
 
@@ -206,7 +210,7 @@ def test_decode_inactive_sequences_untouched():
     check_states(ocfg, s_gpu, state, pre, [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)], "active")
 
 
-@pytest.mark.parametrize("name", ["pace4_g64_int8", "pace48_g32_mixed", "d64_asym_mixed_f32"])
+@pytest.mark.parametrize("name", ["pace4_g64_int8", "pace48_g32_mixed", "d64_asym_mixed_f32", "asym_g64_int8"])
 def test_flush_requant_matches_oracle(name):
     print(f"[flush parity] case={name}", flush=True)
     ocfg, gcfg, state, buffer, _ = make_case(name, seed=300 + len(name))

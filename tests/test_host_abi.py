@@ -111,7 +111,10 @@ def test_validation_errors():
             pace.layout(c)
         assert ei.value.status == pace.PACE_EINVAL, kw
     unsupported = [dict(dk=96, dv=96, group=32), dict(dP=33), dict(Hv=128, Hk=128), dict(chunk=128),
-                   dict(dk=128, dv=64)]
+                   dict(dk=128, dv=64),
+                   # asymmetric 4-bit zero points are packed two a byte within a column, so
+                   # the number of groups per column must be even
+                   dict(group=64, asym=True)]
     for kw in unsupported:
         c = pace.LayerConfig(B=2, Hv=4, Hk=4, dk=64, dv=64, group=32)
         for k, v in kw.items():
