@@ -692,6 +692,402 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------------
+// Warp-specialised variant for bf16 I/O with the column split (two workgroups per
+// (sequence, head)), eight waves.  Waves 0-3 (consumers) own this block's state columns
+// and run the state-dependent chain of each sub-block: keys transposed, K S and Q S,
+// right-hand sides; then the solve and the outputs; then the state update and the
+// rounding.  Waves 4-7 (producers) run beside them: during the consumers' first stage
+// they form the sub-block's Gram and query-key tiles with their decays (A, P) and the
+// inverses of the diagonal blocks, and request the next sub-block's inputs; during the
+// rest (which no longer reads K, Q or V) they store those inputs and the next gates into
+// LDS.  Two workgroup barriers per sub-block (and one before the loops), passed by every
+// wave; neither role leaves its loop early, so the barriers always pair up.
+constexpr int kWsThreads = 512;
+
+template <int D>
+struct SmemWS {
+  static constexpr int LA = kSB + 4;
+  Operands<D, 1> x;                    // K, Q, V, K^T of the current sub-block
+  float A[kSB][LA];                    // beta_t e^{g_t-g_i} k_t.k_i, strictly lower
+  float Ti[kSB / 16][16][20];          // inverses of the diagonal blocks (I + A_ii)
+  float P[kSB][LA];                    // e^{g_t-g_i} q_t.k_i, lower incl. diagonal
+  alignas(16) float g[2][kSB];         // gates by sub-block parity: cumulative log2 decay,
+  alignas(16) float beta[2][kSB];      // beta, e^{g_t}, e^{g_end - g_t}
+  alignas(16) float gam[2][kSB];
+  alignas(16) float wend[2][kSB];
+};
+
+// Producer jobs (token-tile pairs of K K^T and Q K^T, lower triangle), five per producer
+// wave, the first always the diagonal Gram tile (w, w) whose inverse wave w then forms
+// from its own LDS writes.  Entry: {row tile, column tile, query?}.
+constexpr int kWsJobs[4][5][3] = {
+    {{0, 0, 0}, {0, 0, 1}, {3, 0, 0}, {3, 1, 0}, {3, 2, 0}},
+    {{1, 1, 0}, {1, 0, 1}, {1, 1, 1}, {1, 0, 0}, {2, 0, 0}},
+    {{2, 2, 0}, {2, 0, 1}, {2, 1, 1}, {2, 2, 1}, {2, 1, 0}},
+    {{3, 3, 0}, {3, 0, 1}, {3, 1, 1}, {3, 2, 1}, {3, 3, 1}}};
+// job jj of every wave as one constant: byte w = row | column << 2 | query << 4
+constexpr uint32_t ws_job_code(int jj) {
+  uint32_t c = 0;
+  for (int w = 0; w < 4; ++w)
+    c |= (uint32_t)(kWsJobs[w][jj][0] | (kWsJobs[w][jj][1] << 2) | (kWsJobs[w][jj][2] << 4)) << (8 * w);
+  return c;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p) {
+  constexpr int KT = D / 16;           // key tiles
+  constexpr int CT = D / 128;          // column tiles per consumer wave (D / 2 columns)
+  constexpr int TT = kSB / 16;         // token tiles
+  constexpr int JPW = 5;               // producer jobs per wave
+  using I = Inputs<D, 1>;
+  __shared__ SmemWS<D> sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
+  const int tid = threadIdx.x & (kThreads - 1);                         // index within the role
+  const int l16 = lane & 15, qd = lane >> 4;
+  const int tile = blockIdx.x / 2, cb = (blockIdx.x % 2) * (D / 2);   // first column
+  const int b = tile / p.Hv, h = tile % p.Hv, kh = h / p.gamma;
+  const int nsb = (p.T + kSB - 1) / kSB;
+
+  if (wave < 4) {
+    // ===================================================================== consumers
+    const bool is8 = (p.mask8 >> h) & 1ull;
+    const uint64_t below = h ? (p.mask8 & ((1ull << h) - 1ull)) : 0ull;
+    const uint64_t n8 = (uint64_t)__popcll(below);
+    Rec rec;
+    rec.base = p.state + (uint64_t)b * p.seq_stride + (uint64_t)h * p.rec4 + n8 * (p.rec8 - p.rec4);
+    rec.scales = (uint16_t*)(rec.base + (is8 ? p.scales_off8 : p.scales_off4));
+    rec.zeros = rec.base + (is8 ? p.zeros_off8 : p.zeros_off4);
+    rec.bits = is8 ? 8 : 4;
+    rec.NG = D / p.group;
+    rec.asym = p.asym;
+
+    // initial state: dequantise this lane's accumulator entries (all loads first)
+    v4f S[CT][KT];
+    {
+      uint32_t c4[CT][KT];
+      uint16_t sc[CT][KT];
+      uint8_t zb[CT][KT];
+      const int ub = rec.bits;
+      const int sel8 = is8 ? 4 * (qd & 1) : 0;
+      const uint8_t* zsrc = p.asym ? rec.zeros : (const uint8_t*)rec.scales;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int j = cb + 16 * (wave * CT + c) + l16;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const int m = 2 * kt + (qd >> 1);
+          const int u = (m & 3) * (D / 32) + (m >> 2);
+          c4[c][kt] = *(const uint32_t*)(rec.base + (size_t)j * (D * ub / 8) + u * ub + sel8);
+          const int e = j * rec.NG + (16 * kt) / p.group;
+          sc[c][kt] = rec.scales[e];
+          zb[c][kt] = p.asym ? zsrc[is8 ? e : (e >> 1)] : 0;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int j = cb + 16 * (wave * CT + c) + l16;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const int e = j * rec.NG + (16 * kt) / p.group;
+          const float s = bf16_to_f32(sc[c][kt]);
+          int z = 1 << (rec.bits - 1);
+          if (p.asym) z = is8 ? (int)zb[c][kt] : (int)((zb[c][kt] >> (4 * (e & 1))) & 15);
+          const uint32_t w = is8 ? c4[c][kt] : ((c4[c][kt] >> (4 * (qd & 1))) & 0x0F0F0F0Fu);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[c][kt][i] = s * ((float)((w >> (8 * i)) & 0xFFu) - (float)z);
+        }
+      }
+    }
+    __syncthreads();                   // (barrier 0) sub-block 0's inputs and gates in LDS
+
+    for (int sb = 0; sb < nsb; ++sb) {
+      const int t0 = sb * kSB;
+      const int nt = min(kSB, p.T - t0);
+      const int gb = sb & 1;           // gate buffer of this sub-block
+      // keys transposed for the state update
+#pragma unroll
+      for (int it = 0; it < D * (kSB / 8) / kThreads; ++it) {
+        const int pidx = tid + it * kThreads;
+        const int key = pidx % D, blk = pidx / D;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)sm.x.K[8 * blk + 2 * e][key] | ((uint32_t)sm.x.K[8 * blk + 2 * e + 1][key] << 16);
+        *(uint4*)&sm.x.Kt[key][8 * blk] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+
+      // K S and Q S of the sub-block's starting state (state as three bf16 pieces)
+      v4f KS[CT][TT], QS[CT][TT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) KS[c][tt] = QS[c][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int kb = 0; kb < KT / 2; ++kb) {
+          const v4f s0 = S[c][2 * kb], s1 = S[c][2 * kb + 1];
+          v8bf p0, p1, p2;
+          split3(v8f{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]}, p0, p1, p2);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) {
+            const int row = 16 * tt + l16;
+            const v8bf ak = load_2x4(&sm.x.K[row][32 * kb + 4 * qd], &sm.x.K[row][32 * kb + 16 + 4 * qd]);
+            const v8bf aq = load_2x4(&sm.x.Q[row][32 * kb + 4 * qd], &sm.x.Q[row][32 * kb + 16 + 4 * qd]);
+            KS[c][tt] = mfma_bf16(ak, p0, KS[c][tt]);
+            KS[c][tt] = mfma_bf16(ak, p1, KS[c][tt]);
+            KS[c][tt] = mfma_bf16(ak, p2, KS[c][tt]);
+            QS[c][tt] = mfma_bf16(aq, p0, QS[c][tt]);
+            QS[c][tt] = mfma_bf16(aq, p1, QS[c][tt]);
+            QS[c][tt] = mfma_bf16(aq, p2, QS[c][tt]);
+          }
+        }
+      // right-hand sides R = diag(beta) V - diag(beta Gamma) K S
+      v4f R[CT][TT];
+      float4 gam4[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) gam4[tt] = *(const float4*)&sm.gam[gb][16 * tt + 4 * qd];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int j = cb + 16 * (wave * CT + c) + l16;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const float4 bet4 = *(const float4*)&sm.beta[gb][16 * tt + 4 * qd];
+          const float bt[4] = {bet4.x, bet4.y, bet4.z, bet4.w};
+          const float gt[4] = {gam4[tt].x, gam4[tt].y, gam4[tt].z, gam4[tt].w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tt + 4 * qd + r;
+            R[c][tt][r] = bt[r] * fmaf(-gt[r], KS[c][tt][r], bf16_to_f32(sm.x.V[t][j]));
+          }
+        }
+      }
+      __syncthreads();                 // (barrier 1) A, P and the inverses are complete;
+                                       // K, Q and V are no longer read
+
+      // blocked forward solve: U_i = Ti_i (R_i - sum_{j<i} A_ij U_j)
+      v4f U[CT][TT];
+#pragma unroll
+      for (int ib = 0; ib < TT; ++ib) {
+        v4f acc[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[c] = R[c][ib];
+#pragma unroll
+        for (int jb = 0; jb < ib; ++jb) {
+          const float4 av = *(const float4*)&sm.A[16 * ib + l16][16 * jb + 4 * qd];
+          const float na[4] = {-av.x, -av.y, -av.z, -av.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < CT; ++c) acc[c] = mfma4(na[r], U[c][jb][r], acc[c]);
+        }
+        const float4 tv = *(const float4*)&sm.Ti[ib][l16][4 * qd];
+        const float ti[4] = {tv.x, tv.y, tv.z, tv.w};
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          U[c][ib] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) U[c][ib] = mfma4(ti[r], acc[c][r], U[c][ib]);
+        }
+      }
+
+      // outputs O = diag(Gamma) Q S + P U, the four token tiles' P U chains interleaved
+      {
+        v4f O[TT][CT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float gr = r == 0 ? gam4[tt].x : r == 1 ? gam4[tt].y : r == 2 ? gam4[tt].z : gam4[tt].w;
+              O[tt][c][r] = gr * QS[c][tt][r];
+            }
+#pragma unroll
+        for (int ib = 0; ib < TT; ++ib) {
+          float4 px[TT];
+#pragma unroll
+          for (int tt = ib; tt < TT; ++tt) px[tt] = *(const float4*)&sm.P[16 * tt + l16][16 * ib + 4 * qd];
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int tt = ib; tt < TT; ++tt) {
+              const float pv = s == 0 ? px[tt].x : s == 1 ? px[tt].y : s == 2 ? px[tt].z : px[tt].w;
+#pragma unroll
+              for (int c = 0; c < CT; ++c) O[tt][c] = mfma4(pv, U[c][ib][s], O[tt][c]);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int c = 0; c < CT; ++c) {
+            const int j = cb + 16 * (wave * CT + c) + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 16 * tt + 4 * qd + r;
+              if (t < nt) ((uint16_t*)p.o)[(((size_t)b * p.T + t0 + t) * p.Hv + h) * D + j] = f32_to_bf16_rne(O[tt][c][r]);
+            }
+          }
+      }
+
+      // state S' = Gamma_end S + K^T diag(e^{g_end - g}) U
+      {
+        const float ge = sm.gam[gb][kSB - 1];
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) S[c][kt] *= ge;
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int tb = 0; tb < TT / 2; ++tb) {
+            const float4 w0 = *(const float4*)&sm.wend[gb][32 * tb + 4 * qd];
+            const float4 w1 = *(const float4*)&sm.wend[gb][32 * tb + 16 + 4 * qd];
+            const v4f u0 = U[c][2 * tb], u1 = U[c][2 * tb + 1];
+            v8bf p0, p1, p2;
+            split3(v8f{u0[0] * w0.x, u0[1] * w0.y, u0[2] * w0.z, u0[3] * w0.w,
+                       u1[0] * w1.x, u1[1] * w1.y, u1[2] * w1.z, u1[3] * w1.w}, p0, p1, p2);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+              const uint16_t* kr = &sm.x.Kt[16 * kt + l16][0];
+              const v8bf ak = load_2x4(kr + 32 * tb + 4 * qd, kr + 32 * tb + 16 + 4 * qd);
+              S[c][kt] = mfma_bf16(ak, p0, S[c][kt]);
+              S[c][kt] = mfma_bf16(ak, p1, S[c][kt]);
+              S[c][kt] = mfma_bf16(ak, p2, S[c][kt]);
+            }
+          }
+      }
+      // rounding at chunk ends and after the last token
+      const int done = t0 + nt;
+      if (done % p.chunk == 0 || done == p.T) {
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          const int j = cb + 16 * (wave * CT + c) + l16;
+          if (p.group == 64) requant_tile<D, 64>(S[c], rec, j, qd);
+          else requant_tile<D, 32>(S[c], rec, j, qd);
+        }
+      }
+      __syncthreads();                 // (barrier 2) the next sub-block's inputs are in
+                                       // LDS; K^T, A, P and the inverses may be replaced
+    }
+  } else {
+    // ===================================================================== producers
+    const int pw = wave - 4;
+    I in;
+    // this sub-block's inputs (prefetched) and gates into LDS
+    auto store_inputs = [&](int gbuf) {
+#pragma unroll
+      for (int it = 0; it < I::NV; ++it) {
+        const int i = tid + it * kThreads;
+        const int t = i / I::VPR, c = (i % I::VPR) * 8;
+        *(uint4*)&sm.x.K[t][c] = in.k[it];
+        *(uint4*)&sm.x.Q[t][c] = in.q[it];
+        *(uint4*)&sm.x.V[t][c] = in.v[it];
+      }
+      if (pw == 0) {
+        // inclusive scan of log a over the 64 tokens (a = 0 is clamped to e^-80)
+        float x = fmaxf(logf(in.a), -80.f);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const float y = __shfl_up(x, o);
+          if (lane >= o) x += y;
+        }
+        const float gend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+        sm.g[gbuf][lane] = x * 1.4426950408889634f;   // log2 units: decays are exp2 of differences
+        sm.beta[gbuf][lane] = in.beta;
+        sm.gam[gbuf][lane] = expf(x);
+        sm.wend[gbuf][lane] = expf(gend - x);
+      }
+    };
+
+    load_inputs<D, 1>(in, p, b, h, kh, 0, min(kSB, p.T), tid);
+    store_inputs(0);
+    __syncthreads();                   // (barrier 0)
+
+    for (int sb = 0; sb < nsb; ++sb) {
+      const int t0 = sb * kSB;
+      const int gb = sb & 1;
+      const bool more = sb + 1 < nsb;
+      // ------------------------- Gram and query-key tiles of this sub-block -> A, P
+      {
+        v4f acc[JPW];
+        int tis[JPW], tjs[JPW];
+        bool isqs[JPW];
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+          const uint32_t code = (ws_job_code(jj) >> (8 * pw)) & 0xFFu;
+          tis[jj] = code & 3;
+          tjs[jj] = (code >> 2) & 3;
+          isqs[jj] = (code >> 4) & 1;
+          acc[jj] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) {
+          v8bf xa[JPW], xb[JPW];
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj) {
+            const uint16_t* X = isqs[jj] ? &sm.x.Q[16 * tis[jj] + l16][0] : &sm.x.K[16 * tis[jj] + l16][0];
+            xa[jj] = load_8(X + 32 * kb + 8 * qd);
+            xb[jj] = load_8(&sm.x.K[16 * tjs[jj] + l16][32 * kb + 8 * qd]);
+          }
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj) acc[jj] = mfma_bf16(xa[jj], xb[jj], acc[jj]);
+        }
+        // the next sub-block's inputs, requested while these tiles are formed
+        if (more) load_inputs<D, 1>(in, p, b, h, kh, t0 + kSB, min(kSB, p.T - t0 - kSB), tid);
+        float4 g4[JPW], b4[JPW];
+        float gi[JPW];
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+          g4[jj] = *(const float4*)&sm.g[gb][16 * tis[jj] + 4 * qd];
+          b4[jj] = *(const float4*)&sm.beta[gb][16 * tis[jj] + 4 * qd];
+          gi[jj] = sm.g[gb][16 * tjs[jj] + l16];
+        }
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+          const int i = 16 * tjs[jj] + l16;
+          const float gt[4] = {g4[jj].x, g4[jj].y, g4[jj].z, g4[jj].w};
+          const float bt[4] = {b4[jj].x, b4[jj].y, b4[jj].z, b4[jj].w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tis[jj] + 4 * qd + r;
+            // (the hardware exp2: decays under 2^-126 read as 0, far below any fp32 sum)
+            const float dec = __builtin_amdgcn_exp2f(fminf(gt[r] - gi[jj], 0.f));
+            if (isqs[jj]) sm.P[t][i] = t >= i ? dec * acc[jj][r] : 0.f;
+            else sm.A[t][i] = t > i ? bt[r] * dec * acc[jj][r] : 0.f;
+          }
+        }
+      }
+      // ---- inverse of diagonal block pw, written above by this wave (its job 0): a
+      // wave's LDS accesses complete in order, so only the compiler must keep the reads
+      // below the writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      {
+        const int cc = lane & 15, base = 16 * pw;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          float acc = t == cc ? 1.f : 0.f;
+#pragma unroll
+          for (int i = 0; i < t; ++i) acc = fmaf(-sm.A[base + t][base + i], x[i], acc);
+          x[t] = acc;
+        }
+        if (lane < 16) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) sm.Ti[pw][t][cc] = x[t];
+        }
+      }
+      __syncthreads();                 // (barrier 1)
+      if (more) store_inputs(gb ^ 1);
+      __syncthreads();                 // (barrier 2)
+    }
+  }
+}
+
 // Compute units of the current device (one workgroup of this kernel fills a CU's LDS).
 int device_cus() {
   static int cached[64] = {0};
@@ -711,7 +1107,8 @@ void launch_wy(const PrefillParams& p, hipStream_t stream) {
   // when two workgroups per (sequence, head) still run in one round, split the columns
   if constexpr (D >= 128) {
     if (2 * tiles <= (unsigned)device_cus()) {
-      hipLaunchKernelGGL((prefill_wy_kernel<D, IO, 2>), dim3(2 * tiles), dim3(kThreads), 0, stream, p);
+      if constexpr (IO == 1) hipLaunchKernelGGL((prefill_ws_kernel<D>), dim3(2 * tiles), dim3(kWsThreads), 0, stream, p);
+      else hipLaunchKernelGGL((prefill_wy_kernel<D, IO, 2>), dim3(2 * tiles), dim3(kThreads), 0, stream, p);
       return;
     }
   }
