@@ -295,10 +295,10 @@ def prefill_flops(T, Hv, B, d, bf16_io=True, chunk=256, sb=64):
     inputs, bf16 16x16x32 MFMAs for K K^T and Q K^T (one pass) and for K S, Q S and the
     state update (three passes each: the fp32 operand as three bf16 pieces), and fp32
     16x16x4 MFMAs for the blocked solve and P U; with fp32 inputs, all fp32 16x16x4.
-    When twice the pairs fit the CUs (256 on MI355X) at d >= 128, the library splits each
-    pair over two column-block workgroups, which both issue the key-side products
-    (K K^T, Q K^T)."""
-    cs = 2 if (d >= 128 and 2 * B * Hv <= 256) else 1
+    At d >= 128 the library splits each pair over two column-block workgroups (always with
+    bf16 inputs; with fp32 inputs when twice the pairs fit the 256 CUs of MI355X), which
+    both issue the key-side products (K K^T, Q K^T)."""
+    cs = 2 if (d >= 128 and (bf16_io or 2 * B * Hv <= 256)) else 1
     C = chunk
     per_chunk = 2 * (2.5 * C * C * d + 3 * C * d * d + C ** 3 / 6)
     alg = per_chunk * (-(-T // C)) * B * Hv
@@ -355,7 +355,7 @@ def run_long_prefill(torch, pace, args):
            "mfma_util_of_dtype_peak": util,
            "note": "bf16 figures count the three split passes of the fp32 operands (exact bf16 "
                    "inputs times the state / decayed U as three bf16 pieces)",
-           "workgroups": B * Hv * (2 if (d >= 128 and 2 * B * Hv <= 256) else 1)}
+           "workgroups": B * Hv * (2 if d >= 128 else 1), "threads_per_workgroup": 512 if d >= 128 else 256}
     log(f"long prefill: {ms:.2f} ms, {res['tokens_per_s']:,.0f} tok/s, executed "
         f"bf16 {res['executed_TFLOPs']['bf16']} TFLOP/s ({util['bf16']:.3f} of peak), "
         f"f32 {res['executed_TFLOPs']['f32']} TFLOP/s ({util['f32']:.3f} of peak), "

@@ -1104,15 +1104,21 @@ int device_cus() {
 template <int D, int IO>
 void launch_wy(const PrefillParams& p, hipStream_t stream) {
   const unsigned tiles = (unsigned)p.B * (unsigned)p.Hv;
-  // when two workgroups per (sequence, head) still run in one round, split the columns
-  if constexpr (D >= 128) {
-    if (2 * tiles <= (unsigned)device_cus()) {
-      if constexpr (IO == 1) hipLaunchKernelGGL((prefill_ws_kernel<D>), dim3(2 * tiles), dim3(kWsThreads), 0, stream, p);
-      else hipLaunchKernelGGL((prefill_wy_kernel<D, IO, 2>), dim3(2 * tiles), dim3(kThreads), 0, stream, p);
-      return;
+  if constexpr (D >= 128 && IO == 1) {
+    // bf16 I/O: the warp-specialised kernel, two column-block workgroups per (sequence,
+    // head) whatever the number of pairs
+    hipLaunchKernelGGL((prefill_ws_kernel<D>), dim3(2 * tiles), dim3(kWsThreads), 0, stream, p);
+  } else {
+    // fp32 I/O at d = 128: split the columns when two workgroups per pair still run in
+    // one round
+    if constexpr (D >= 128) {
+      if (2 * tiles <= (unsigned)device_cus()) {
+        hipLaunchKernelGGL((prefill_wy_kernel<D, IO, 2>), dim3(2 * tiles), dim3(kThreads), 0, stream, p);
+        return;
+      }
     }
+    hipLaunchKernelGGL((prefill_wy_kernel<D, IO, 1>), dim3(tiles), dim3(kThreads), 0, stream, p);
   }
-  hipLaunchKernelGGL((prefill_wy_kernel<D, IO, 1>), dim3(tiles), dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace
