@@ -34,6 +34,8 @@
 // into registers while the current one is computed.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "pace_internal.h"
 #include "pace_numerics.h"
 
@@ -1024,17 +1026,29 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
           isqs[jj] = (code >> 4) & 1;
           acc[jj] = v4f{0.f, 0.f, 0.f, 0.f};
         }
+        // per 32-key block, the four key tiles and this wave's query tile are each read
+        // once and shared by the five jobs (LDS reads are what the consumers' stage
+        // contends for); the job tiles are compile-time values per wave
+        auto gram_mma = [&](auto pwc) {
+          constexpr int PW = decltype(pwc)::value;
 #pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb) {
-          v8bf xa[JPW], xb[JPW];
+          for (int kb = 0; kb < D / 32; ++kb) {
+            v8bf kx[TT];
 #pragma unroll
-          for (int jj = 0; jj < JPW; ++jj) {
-            const uint16_t* X = isqs[jj] ? &sm.x.Q[16 * tis[jj] + l16][0] : &sm.x.K[16 * tis[jj] + l16][0];
-            xa[jj] = load_8(X + 32 * kb + 8 * qd);
-            xb[jj] = load_8(&sm.x.K[16 * tjs[jj] + l16][32 * kb + 8 * qd]);
+            for (int t = 0; t < TT; ++t) kx[t] = load_8(&sm.x.K[16 * t + l16][32 * kb + 8 * qd]);
+            const v8bf qx = load_8(&sm.x.Q[16 * PW + l16][32 * kb + 8 * qd]);
+#pragma unroll
+            for (int jj = 0; jj < JPW; ++jj) {
+              const v8bf xa = kWsJobs[PW][jj][2] ? qx : kx[kWsJobs[PW][jj][0]];
+              acc[jj] = mfma_bf16(xa, kx[kWsJobs[PW][jj][1]], acc[jj]);
+            }
           }
-#pragma unroll
-          for (int jj = 0; jj < JPW; ++jj) acc[jj] = mfma_bf16(xa[jj], xb[jj], acc[jj]);
+        };
+        switch (pw) {
+          case 0: gram_mma(std::integral_constant<int, 0>{}); break;
+          case 1: gram_mma(std::integral_constant<int, 1>{}); break;
+          case 2: gram_mma(std::integral_constant<int, 2>{}); break;
+          default: gram_mma(std::integral_constant<int, 3>{}); break;
         }
         // the next sub-block's inputs, requested while these tiles are formed
         if (more) load_inputs<D, 1>(in, p, b, h, kh, t0 + kSB, min(kSB, p.T - t0 - kSB), tid);
