@@ -81,6 +81,21 @@ def test_prefill_chunks_match_oracle(name):
     check_prefill_call(ocfg, gcfg, s1, toks.span(256, 356), tiles, name + "/partial")
 
 
+@pytest.mark.parametrize("T", [1, 5, 64, 65])
+def test_prefill_short_prompts(T):
+    """Prompts of at most one 64-token sub-block and just past it (one sub-block, so the
+    producer waves of the bf16 kernel prepare nothing after the first; a second holding a
+    single token), starting from a non-zero rounded state: outputs and the state rounded
+    after the last token match the oracle."""
+    print(f"[prefill parity] short prompt T={T}", flush=True)
+    ocfg, gcfg = cfgs("pace48_g32_bf16")
+    toks = make_tokens(900 + T, ocfg.B, 256 + T, ocfg.Hv, ocfg.Hk, ocfg.dk, ocfg.dv, bf16=True)
+    tiles = [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)]
+    zero = np.zeros(pk.state_layout(ocfg)[2], dtype=np.uint8)
+    _, s1, _ = pk.prefill_layer(ocfg, zero, *toks.span(0, 256), tiles=tiles)
+    check_prefill_call(ocfg, gcfg, s1, toks.span(256, 256 + T), tiles, f"short T={T}")
+
+
 def test_prefill_multi_chunk_call_equals_separate_calls():
     print("[prefill] multi-chunk self-consistency", flush=True)
     ocfg, gcfg = cfgs("pace48_g32_bf16")
