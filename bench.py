@@ -469,13 +469,13 @@ def main():
     if args.sweep:
         sweep = []
         for Bs in [int(x) for x in args.sweep_batches.split(",")]:
-            rs = run_decode(torch, pace, args, Bs, max(3, args.steps // 2), 2)
+            rs = run_decode(torch, pace, args, Bs, max(3, args.steps // 2), args.warmup)
             ent = {"B": Bs, "tokens_per_s": round(rs["tokens_per_s"], 1), "GBps": round(rs["achieved"], 1),
                    "mean_launch_us": round(rs["launch_us"], 3),
                    "working_set_MB": round((rs["L"]["state_bytes"] + rs["L"]["buffer_bytes"]) * Lyr / 1e6, 1)}
             if args.baseline:
                 bl = run_bf16_baseline(torch, pace, args, rs["cfg"], rs["layers"], steps=max(3, args.steps // 2),
-                                       warmup=2, split=False)
+                                       warmup=args.warmup, split=False)
                 ent["bf16_tokens_per_s"] = bl["value"]
                 ent["bf16_GBps"] = bl["timed_region_GBps"]
                 ent["speedup_vs_bf16"] = round(rs["tokens_per_s"] / bl["value"], 3)

@@ -14,6 +14,8 @@
 namespace pace {
 namespace {
 
+typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 
 template <int LPC>
@@ -47,7 +49,10 @@ __global__ __launch_bounds__(kThreads) void bf16_decode_kernel(Bf16Params p) {
   for (int pass = 0; pass < PASSES; ++pass) {
     const int j = pass * CPB + wave * CPW + lane / LPC;
     uint4* src = (uint4*)(tile + (size_t)j * D + 8 * m);
-    const uint4 raw = *src;
+    // the state is a stream (read and written once per launch): non-temporal accesses keep
+    // it from displacing reused data, as in the int4 kernel
+    const v4u32 rv = __builtin_nontemporal_load((const v4u32*)src);
+    const uint4 raw = make_uint4(rv.x, rv.y, rv.z, rv.w);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     float s[8];
 #pragma unroll
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void bf16_decode_kernel(Bf16Params p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       outw[e] = (uint32_t)f32_to_bf16_rne(s[2 * e]) | ((uint32_t)f32_to_bf16_rne(s[2 * e + 1]) << 16);
-    *src = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    __builtin_nontemporal_store(v4u32{outw[0], outw[1], outw[2], outw[3]}, (v4u32*)src);
     oq = seg_sum<LPC>(oq);
     if (m == 0) {
       if (kBf16) ((uint16_t*)p.o)[vi] = f32_to_bf16_rne(oq);

@@ -45,6 +45,50 @@ constexpr int kThreads = 64 * kWaves;
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
+typedef unsigned v2u32 __attribute__((ext_vector_type(2)));
+
+// The packed state is a stream: a launch reads each tile's codes, scales and zero points
+// once, writes them only on the flush, and reads nothing of them again.  When the states
+// of a model's layers together exceed the last-level cache (large batches: 17.8 MB a
+// layer at B = 64, 427 MB over 24 layers), its loads and stores are non-temporal (NTS), so
+// that the stream does not push out of the caches the data that is reused: above all the
+// decode buffer, which every step of the period reads again, and the key token and
+// buffered keys that the value heads of one key head share.  Small batches keep ordinary
+// accesses, so that the states stay cache-resident from one step to the next.
+template <bool NT>
+__device__ inline uint4 ld_state(const void* p) {
+  if constexpr (NT) {
+    const v4u32 v = __builtin_nontemporal_load((const v4u32*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *(const uint4*)p;
+  }
+}
+template <bool NT>
+__device__ inline uint2 ld_state2(const void* p) {
+  if constexpr (NT) {
+    const v2u32 v = __builtin_nontemporal_load((const v2u32*)p);
+    return make_uint2(v.x, v.y);
+  } else {
+    return *(const uint2*)p;
+  }
+}
+template <bool NT, class T>
+__device__ inline void st_state(T* p, T v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+template <bool NT>
+__device__ inline void st_state4(void* p, uint4 w) {
+  if constexpr (NT) __builtin_nontemporal_store(v4u32{w.x, w.y, w.z, w.w}, (v4u32*)p);
+  else *(uint4*)p = w;
+}
+template <bool NT>
+__device__ inline void st_state2(void* p, uint2 w) {
+  if constexpr (NT) __builtin_nontemporal_store(v2u32{w.x, w.y}, (v2u32*)p);
+  else *(uint2*)p = w;
+}
 
 template <bool BF16>
 __device__ inline float load_io(const void* p, size_t i) {
@@ -130,7 +174,8 @@ struct alignas(16) Smem {
 // IO: 1 = bf16 q/k/v/o, 0 = fp32.
 // GT: scale-group size (32 or 64), 0 = taken from the parameters at run time.
 // AS: 0 = symmetric, 1 = asymmetric, 2 = taken from the parameters at run time.
-template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS>
+// NTS: the state's codes, scales and zero points are read and written non-temporally.
+template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS>
 // Eight resident workgroups per CU (four waves per SIMD) for the specialised dP <= 8
 // variants, so a 2048-tile launch runs in one round: at most 128 VGPRs.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOK <= 8 && GT != 0 ? 4 : 1)))
@@ -232,8 +277,8 @@ void decode_kernel(DecodeParams p) {
   // instead of a zero-point region they do not have)
   const int sc_vec = D * NG * 2 / 16;
   const int zp_vec = asym ? D * NG * bits / 8 / 16 : 1;
-  const uint4 sc_reg = ((const uint4*)g_scales)[min(tid, sc_vec - 1)];
-  const uint4 zp_reg = ((const uint4*)(asym ? (const uint8_t*)g_zeros : (const uint8_t*)g_scales))[min(tid, zp_vec - 1)];
+  const uint4 sc_reg = ld_state<NTS>((const uint4*)g_scales + min(tid, sc_vec - 1));
+  const uint4 zp_reg = ld_state<NTS>((const uint4*)(asym ? (const uint8_t*)g_zeros : (const uint8_t*)g_scales) + min(tid, zp_vec - 1));
 
   // counts outside [0, dP) cannot come from this library; clamp so that every slot
   // index stays inside the buffer whatever the buffer holds
@@ -434,16 +479,16 @@ void decode_kernel(DecodeParams p) {
     const uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
     if (!is8) {
       if constexpr (KB == 4) {
-        const uint4 v = *(const uint4*)colp;
+        const uint4 v = ld_state<NTS>(colp);
         araw[s][0] = v.x; araw[s][1] = v.y; araw[s][2] = v.z; araw[s][3] = v.w;
       } else {
-        const uint2 v = *(const uint2*)colp;
+        const uint2 v = ld_state2<NTS>(colp);
         araw[s][0] = v.x; araw[s][1] = v.y;
       }
     } else if constexpr (HB != 4) {
 #pragma unroll
       for (int kb = 0; kb < KB; kb += 2) {
-        const uint4 v = *(const uint4*)(colp + kb * 8);
+        const uint4 v = ld_state<NTS>(colp + kb * 8);
         araw[s][2 * kb] = v.x; araw[s][2 * kb + 1] = v.y; araw[s][2 * kb + 2] = v.z; araw[s][2 * kb + 3] = v.w;
       }
     }
@@ -767,16 +812,16 @@ void decode_kernel(DecodeParams p) {
       if (asym) zg[g] = __builtin_amdgcn_ds_bpermute(qaddr + 64 * g, gq.z);
     }
     if (qq < NG) {
-      g_scales[c * NG + qq] = (uint16_t)(f32_bits(gq.s) >> 16);
+      st_state<NTS>(&g_scales[c * NG + qq], (uint16_t)(f32_bits(gq.s) >> 16));
       if (asym) {
         const int e = c * NG + qq;
         if (is8) {
-          g_zeros[e] = (uint8_t)gq.z;
+          st_state<NTS>(&g_zeros[e], (uint8_t)gq.z);
         } else if (e & 1) {                 // two 4-bit zero points a byte, low nibble first
           int zlo = zg[0];
 #pragma unroll
           for (int g = 1; g < 4; ++g) zlo = g == qq - 1 ? zg[g] : zlo;
-          g_zeros[e >> 1] = (uint8_t)(zlo | (gq.z << 4));
+          st_state<NTS>(&g_zeros[e >> 1], (uint8_t)(zlo | (gq.z << 4)));
         }
       }
     }
@@ -816,30 +861,42 @@ void decode_kernel(DecodeParams p) {
     }
     uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
     if (!is8) {
-      if constexpr (KB == 4) *(uint4*)colp = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-      else *(uint2*)colp = make_uint2(outw[0], outw[1]);
+      if constexpr (KB == 4) st_state4<NTS>(colp, make_uint4(outw[0], outw[1], outw[2], outw[3]));
+      else st_state2<NTS>(colp, make_uint2(outw[0], outw[1]));
     } else if constexpr (HB != 4) {
 #pragma unroll
       for (int kb = 0; kb < KB; kb += 2)
-        *(uint4*)(colp + kb * 8) = make_uint4(outw[2 * kb], outw[2 * kb + 1], outw[2 * kb + 2], outw[2 * kb + 3]);
+        st_state4<NTS>(colp + kb * 8, make_uint4(outw[2 * kb], outw[2 * kb + 1], outw[2 * kb + 2], outw[2 * kb + 3]));
     }
   }
   if (tid == 0) *countp = 0;
 }
 
-template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS>
+template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS = false>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, TOK, BUF, HB, IO, GT, AS>), dim3((unsigned)p.Hv, (unsigned)p.B), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<D, TOK, BUF, HB, IO, GT, AS, NTS>), dim3((unsigned)p.Hv, (unsigned)p.B), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
+
+// Layers whose packed states (all sequences) reach this size stream them with
+// non-temporal accesses: a stack of 24-32 such layers no longer fits the 256 MB
+// last-level cache of MI355X, so the states would only evict the reused data.  Measured
+// on the 24-layer PACE-4 stack: B = 16 (4.4 MB a layer) is 5% faster with ordinary
+// accesses, B = 32 (8.9 MB) the same either way, B = 64 (17.8 MB) 11% faster streamed.
+constexpr uint64_t kStreamStateBytes = 8ull << 20;
 
 // Specialised instantiations for the layouts the method names (d = 128, dP <= 8, bf16
 // I/O; 64-key symmetric and 32-key asymmetric groups, and their mirror images), with
 // group size and symmetry known at compile time.
+template <int BUF, int HB, bool NT>
+hipError_t launch_fast_nt(const DecodeParams& p, hipStream_t stream) {
+  if (p.group == 64) return p.asym ? launch_t<128, 8, BUF, HB, 1, 64, 1, NT>(p, stream) : launch_t<128, 8, BUF, HB, 1, 64, 0, NT>(p, stream);
+  return p.asym ? launch_t<128, 8, BUF, HB, 1, 32, 1, NT>(p, stream) : launch_t<128, 8, BUF, HB, 1, 32, 0, NT>(p, stream);
+}
 template <int BUF, int HB>
 hipError_t launch_fast(const DecodeParams& p, hipStream_t stream) {
-  if (p.group == 64) return p.asym ? launch_t<128, 8, BUF, HB, 1, 64, 1>(p, stream) : launch_t<128, 8, BUF, HB, 1, 64, 0>(p, stream);
-  return p.asym ? launch_t<128, 8, BUF, HB, 1, 32, 1>(p, stream) : launch_t<128, 8, BUF, HB, 1, 32, 0>(p, stream);
+  const bool stream_state = (uint64_t)p.B * p.seq_stride >= kStreamStateBytes;
+  return stream_state ? launch_fast_nt<BUF, HB, true>(p, stream) : launch_fast_nt<BUF, HB, false>(p, stream);
 }
 
 template <int D, int BUF, int IO>
