@@ -25,7 +25,9 @@ __device__ inline float seg_sum(float x) {
   return x;
 }
 
-template <int D, int IO>
+// NTS: the state is read and written non-temporally (chosen by state size, as for the
+// int4 kernel).
+template <int D, int IO, bool NTS>
 __global__ __launch_bounds__(kThreads) void bf16_decode_kernel(Bf16Params p) {
   constexpr int LPC = D / 8;                 // lanes per column
   constexpr int CPW = 64 / LPC;              // columns per wave per pass
@@ -49,10 +51,15 @@ __global__ __launch_bounds__(kThreads) void bf16_decode_kernel(Bf16Params p) {
   for (int pass = 0; pass < PASSES; ++pass) {
     const int j = pass * CPB + wave * CPW + lane / LPC;
     uint4* src = (uint4*)(tile + (size_t)j * D + 8 * m);
-    // the state is a stream (read and written once per launch): non-temporal accesses keep
-    // it from displacing reused data, as in the int4 kernel
-    const v4u32 rv = __builtin_nontemporal_load((const v4u32*)src);
-    const uint4 raw = make_uint4(rv.x, rv.y, rv.z, rv.w);
+    // the state is a stream (read and written once per launch); when it is large,
+    // non-temporal accesses keep it from displacing reused data, as in the int4 kernel
+    uint4 raw;
+    if constexpr (NTS) {
+      const v4u32 rv = __builtin_nontemporal_load((const v4u32*)src);
+      raw = make_uint4(rv.x, rv.y, rv.z, rv.w);
+    } else {
+      raw = *src;
+    }
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     float s[8];
 #pragma unroll
@@ -77,7 +84,8 @@ __global__ __launch_bounds__(kThreads) void bf16_decode_kernel(Bf16Params p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       outw[e] = (uint32_t)f32_to_bf16_rne(s[2 * e]) | ((uint32_t)f32_to_bf16_rne(s[2 * e + 1]) << 16);
-    __builtin_nontemporal_store(v4u32{outw[0], outw[1], outw[2], outw[3]}, (v4u32*)src);
+    if constexpr (NTS) __builtin_nontemporal_store(v4u32{outw[0], outw[1], outw[2], outw[3]}, (v4u32*)src);
+    else *src = make_uint4(outw[0], outw[1], outw[2], outw[3]);
     oq = seg_sum<LPC>(oq);
     if (m == 0) {
       if (kBf16) ((uint16_t*)p.o)[vi] = f32_to_bf16_rne(oq);
@@ -92,12 +100,24 @@ hipError_t launch_bf16_decode(const Bf16Params& p, int dk, int dv, int io_bf16,
                               hipStream_t stream) {
   (void)dv;
   const unsigned grid = (unsigned)p.B * (unsigned)p.Hv;
+  // the same rule as the int4 kernel: stream the state once a layer's state reaches 8 MiB
+  const bool nts = (uint64_t)p.B * p.Hv * dk * dk * 2 >= (8ull << 20);
   if (dk == 128) {
-    if (io_bf16) hipLaunchKernelGGL((bf16_decode_kernel<128, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((bf16_decode_kernel<128, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+    if (io_bf16) {
+      if (nts) hipLaunchKernelGGL((bf16_decode_kernel<128, 1, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+      else hipLaunchKernelGGL((bf16_decode_kernel<128, 1, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    } else {
+      if (nts) hipLaunchKernelGGL((bf16_decode_kernel<128, 0, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+      else hipLaunchKernelGGL((bf16_decode_kernel<128, 0, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    }
   } else {
-    if (io_bf16) hipLaunchKernelGGL((bf16_decode_kernel<64, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((bf16_decode_kernel<64, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+    if (io_bf16) {
+      if (nts) hipLaunchKernelGGL((bf16_decode_kernel<64, 1, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+      else hipLaunchKernelGGL((bf16_decode_kernel<64, 1, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    } else {
+      if (nts) hipLaunchKernelGGL((bf16_decode_kernel<64, 0, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+      else hipLaunchKernelGGL((bf16_decode_kernel<64, 0, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }
