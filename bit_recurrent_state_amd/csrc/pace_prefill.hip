@@ -175,6 +175,7 @@ __device__ inline void put8(float* dst, uint4 w) {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v8f __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf16_t __attribute__((ext_vector_type(4)));
 
 __device__ inline v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -196,6 +197,18 @@ __device__ inline v8bf load_2x4(const uint16_t* lo, const uint16_t* hi) {
   const uint4 w = make_uint4(a.x, a.y, b.x, b.y);
   v8bf r;
   __builtin_memcpy(&r, &w, 16);
+  return r;
+}
+
+// Two transposing LDS reads (ds_read_b64_tr_b16) as one MFMA operand: within each group
+// of 16 lanes, lane i receives element i % 4 of the 4-element pieces addressed by lanes
+// i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12 of its group.
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+__device__ inline v8bf load_tr16_2x4(const uint16_t* lo, const uint16_t* hi) {
+  typedef __attribute__((address_space(3))) v4s16* lds_v4s16;
+  const v4s16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16)lo);
+  const v4s16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16)hi);
+  const v8bf r = __builtin_shufflevector(__builtin_bit_cast(v4bf16_t, a), __builtin_bit_cast(v4bf16_t, b), 0, 1, 2, 3, 4, 5, 6, 7);
   return r;
 }
 
@@ -697,20 +710,25 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
 // ------------------------------------------------------------------------------------
 // Warp-specialised variant for bf16 I/O with the column split (two workgroups per
 // (sequence, head)), eight waves.  Waves 0-3 (consumers) own this block's state columns
-// and run the state-dependent chain of each sub-block: keys transposed, K S and Q S,
-// right-hand sides; then the solve and the outputs; then the state update and the
+// and run the state-dependent chain of each sub-block: K S and Q S, right-hand sides;
+// then the solve and the outputs; then the state update, whose K^T operand is read
+// transposed straight from the row-major key tile (ds_read_b64_tr_b16); then the
 // rounding.  Waves 4-7 (producers) run beside them: during the consumers' first stage
 // they form the sub-block's Gram and query-key tiles with their decays (A, P) and the
 // inverses of the diagonal blocks, and request the next sub-block's inputs; during the
-// rest (which no longer reads K, Q or V) they store those inputs and the next gates into
-// LDS.  Two workgroup barriers per sub-block (and one before the loops), passed by every
+// rest (which no longer reads Q or V, and reads the keys of the other parity) they store
+// those inputs and the next gates into LDS.  Two workgroup barriers per sub-block (and one before the loops), passed by every
 // wave; neither role leaves its loop early, so the barriers always pair up.
 constexpr int kWsThreads = 512;
 
 template <int D>
 struct SmemWS {
   static constexpr int LA = kSB + 4;
-  Operands<D, 1> x;                    // K, Q, V, K^T of the current sub-block
+  static constexpr int LD = D + 8;     // bf16 row stride: 16-byte aligned rows
+  uint16_t K[2][kSB][LD];              // keys by sub-block parity (the state update of one
+                                       // sub-block reads them while the next ones arrive)
+  uint16_t Q[kSB][LD];                 // queries and values of the current sub-block
+  uint16_t V[kSB][LD];
   float A[kSB][LA];                    // beta_t e^{g_t-g_i} k_t.k_i, strictly lower
   float Ti[kSB / 16][16][20];          // inverses of the diagonal blocks (I + A_ii)
   float P[kSB][LA];                    // e^{g_t-g_i} q_t.k_i, lower incl. diagonal
@@ -809,18 +827,6 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
       const int t0 = sb * kSB;
       const int nt = min(kSB, p.T - t0);
       const int gb = sb & 1;           // gate buffer of this sub-block
-      // keys transposed for the state update
-#pragma unroll
-      for (int it = 0; it < D * (kSB / 8) / kThreads; ++it) {
-        const int pidx = tid + it * kThreads;
-        const int key = pidx % D, blk = pidx / D;
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = (uint32_t)sm.x.K[8 * blk + 2 * e][key] | ((uint32_t)sm.x.K[8 * blk + 2 * e + 1][key] << 16);
-        *(uint4*)&sm.x.Kt[key][8 * blk] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-
       // K S and Q S of the sub-block's starting state (state as three bf16 pieces)
       v4f KS[CT][TT], QS[CT][TT];
 #pragma unroll
@@ -837,8 +843,8 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) {
             const int row = 16 * tt + l16;
-            const v8bf ak = load_2x4(&sm.x.K[row][32 * kb + 4 * qd], &sm.x.K[row][32 * kb + 16 + 4 * qd]);
-            const v8bf aq = load_2x4(&sm.x.Q[row][32 * kb + 4 * qd], &sm.x.Q[row][32 * kb + 16 + 4 * qd]);
+            const v8bf ak = load_2x4(&sm.K[gb][row][32 * kb + 4 * qd], &sm.K[gb][row][32 * kb + 16 + 4 * qd]);
+            const v8bf aq = load_2x4(&sm.Q[row][32 * kb + 4 * qd], &sm.Q[row][32 * kb + 16 + 4 * qd]);
             KS[c][tt] = mfma_bf16(ak, p0, KS[c][tt]);
             KS[c][tt] = mfma_bf16(ak, p1, KS[c][tt]);
             KS[c][tt] = mfma_bf16(ak, p2, KS[c][tt]);
@@ -863,7 +869,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = 16 * tt + 4 * qd + r;
-            R[c][tt][r] = bt[r] * fmaf(-gt[r], KS[c][tt][r], bf16_to_f32(sm.x.V[t][j]));
+            R[c][tt][r] = bt[r] * fmaf(-gt[r], KS[c][tt][r], bf16_to_f32(sm.V[t][j]));
           }
         }
       }
@@ -954,8 +960,13 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
                        u1[0] * w1.x, u1[1] * w1.y, u1[2] * w1.z, u1[3] * w1.w}, p0, p1, p2);
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-              const uint16_t* kr = &sm.x.Kt[16 * kt + l16][0];
-              const v8bf ak = load_2x4(kr + 32 * tb + 4 * qd, kr + 32 * tb + 16 + 4 * qd);
+              // keys 16 kt + l16, tokens 32 tb + 4 qd + (0..3) and 32 tb + 16 + 4 qd + (0..3),
+              // read transposed from the row-major key tile: within each 16-lane group,
+              // lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+              // i / 4 + 4 j (j = 0..3), so lane l16 addresses token row + l16 / 4, keys
+              // 16 kt + 4 (l16 % 4) .. + 3
+              const uint16_t* kr = &sm.K[gb][32 * tb + 4 * qd + l16 / 4][16 * kt + 4 * (l16 % 4)];
+              const v8bf ak = load_tr16_2x4(kr, kr + 16 * SmemWS<D>::LD);
               S[c][kt] = mfma_bf16(ak, p0, S[c][kt]);
               S[c][kt] = mfma_bf16(ak, p1, S[c][kt]);
               S[c][kt] = mfma_bf16(ak, p2, S[c][kt]);
@@ -973,7 +984,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
         }
       }
       __syncthreads();                 // (barrier 2) the next sub-block's inputs are in
-                                       // LDS; K^T, A, P and the inverses may be replaced
+                                       // LDS; A, P and the inverses may be replaced
     }
   } else {
     // ===================================================================== producers
@@ -985,9 +996,9 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
       for (int it = 0; it < I::NV; ++it) {
         const int i = tid + it * kThreads;
         const int t = i / I::VPR, c = (i % I::VPR) * 8;
-        *(uint4*)&sm.x.K[t][c] = in.k[it];
-        *(uint4*)&sm.x.Q[t][c] = in.q[it];
-        *(uint4*)&sm.x.V[t][c] = in.v[it];
+        *(uint4*)&sm.K[gbuf][t][c] = in.k[it];
+        *(uint4*)&sm.Q[t][c] = in.q[it];
+        *(uint4*)&sm.V[t][c] = in.v[it];
       }
       if (pw == 0) {
         // inclusive scan of log a over the 64 tokens (a = 0 is clamped to e^-80)
@@ -1035,8 +1046,8 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
           for (int kb = 0; kb < D / 32; ++kb) {
             v8bf kx[TT];
 #pragma unroll
-            for (int t = 0; t < TT; ++t) kx[t] = load_8(&sm.x.K[16 * t + l16][32 * kb + 8 * qd]);
-            const v8bf qx = load_8(&sm.x.Q[16 * PW + l16][32 * kb + 8 * qd]);
+            for (int t = 0; t < TT; ++t) kx[t] = load_8(&sm.K[gb][16 * t + l16][32 * kb + 8 * qd]);
+            const v8bf qx = load_8(&sm.Q[16 * PW + l16][32 * kb + 8 * qd]);
 #pragma unroll
             for (int jj = 0; jj < JPW; ++jj) {
               const v8bf xa = kWsJobs[PW][jj][2] ? qx : kx[kWsJobs[PW][jj][0]];
