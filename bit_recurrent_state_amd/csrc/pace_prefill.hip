@@ -64,7 +64,7 @@ template <int D>
 __device__ inline uint8_t* unit_ptr(const Rec& r, int j, int m) {
   constexpr int KB = D / 32;
   const int u = (m & 3) * KB + (m >> 2);
-  return r.base + (size_t)j * (D * r.bits / 8) + u * r.bits;
+  return r.base + (uint32_t)(j * (D * r.bits / 8) + u * r.bits);   // (a 32-bit per-lane offset)
 }
 
 template <int D>
@@ -710,12 +710,13 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillParams p) {
 // ------------------------------------------------------------------------------------
 // Warp-specialised variant for bf16 I/O with the column split (two workgroups per
 // (sequence, head)), eight waves.  Waves 0-3 (consumers) own this block's state columns
-// and run the state-dependent chain of each sub-block: K S and Q S, right-hand sides;
-// then the solve and the outputs; then the state update, whose K^T operand is read
-// transposed straight from the row-major key tile (ds_read_b64_tr_b16); then the
-// rounding.  Waves 4-7 (producers) run beside them: during the consumers' first stage
-// they form the sub-block's Gram and query-key tiles with their decays (A, P) and the
-// inverses of the diagonal blocks, and request the next sub-block's inputs; during the
+// and run the state-dependent chain of each sub-block: K S and Q S, with the query-key
+// tiles P from the same operands, right-hand sides; then the solve and the outputs; then
+// the state update, whose K^T operand is read transposed straight from the row-major key
+// tile (ds_read_b64_tr_b16); then the rounding.  Waves 4-7 (producers) run beside them:
+// during the consumers' first stage they form the sub-block's Gram tiles with their
+// decays (A) and the inverses of the diagonal blocks, and request the next sub-block's
+// inputs; during the
 // rest (which no longer reads Q or V, and reads the keys of the other parity) they store
 // those inputs and the next gates into LDS.  Two workgroup barriers per sub-block (and one before the loops), passed by every
 // wave; neither role leaves its loop early, so the barriers always pair up.
@@ -738,28 +739,22 @@ struct SmemWS {
   alignas(16) float wend[2][kSB];
 };
 
-// Producer jobs (token-tile pairs of K K^T and Q K^T, lower triangle), five per producer
-// wave, the first always the diagonal Gram tile (w, w) whose inverse wave w then forms
-// from its own LDS writes.  Entry: {row tile, column tile, query?}.
-constexpr int kWsJobs[4][5][3] = {
-    {{0, 0, 0}, {0, 0, 1}, {3, 0, 0}, {3, 1, 0}, {3, 2, 0}},
-    {{1, 1, 0}, {1, 0, 1}, {1, 1, 1}, {1, 0, 0}, {2, 0, 0}},
-    {{2, 2, 0}, {2, 0, 1}, {2, 1, 1}, {2, 2, 1}, {2, 1, 0}},
-    {{3, 3, 0}, {3, 0, 1}, {3, 1, 1}, {3, 2, 1}, {3, 3, 1}}};
-// job jj of every wave as one constant: byte w = row | column << 2 | query << 4
-constexpr uint32_t ws_job_code(int jj) {
-  uint32_t c = 0;
-  for (int w = 0; w < 4; ++w)
-    c |= (uint32_t)(kWsJobs[w][jj][0] | (kWsJobs[w][jj][1] << 2) | (kWsJobs[w][jj][2] << 4)) << (8 * w);
-  return c;
-}
+// Token-tile pairs (row tile, column tile) of the lower triangle, split over the waves:
+// the producers form the Gram tiles A (wave w's first pair is the diagonal (w, w), whose
+// inverse it then forms from its own LDS writes); the consumers form the query-key tiles
+// P from the key and query tiles they already hold for K S and Q S.  -1: no job.
+constexpr int kKkJobs[4][3][2] = {{{0, 0}, {3, 0}, {3, 1}}, {{1, 1}, {1, 0}, {2, 0}},
+                                  {{2, 2}, {2, 1}, {3, 2}}, {{3, 3}, {-1, -1}, {-1, -1}}};
+constexpr int kKkCount[4] = {3, 3, 3, 1};
+constexpr int kQkJobs[4][3][2] = {{{0, 0}, {1, 0}, {1, 1}}, {{2, 0}, {2, 1}, {2, 2}},
+                                  {{3, 0}, {3, 1}, {-1, -1}}, {{3, 2}, {3, 3}, {-1, -1}}};
+constexpr int kQkCount[4] = {3, 3, 2, 2};
 
 template <int D>
 __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p) {
   constexpr int KT = D / 16;           // key tiles
   constexpr int CT = D / 128;          // column tiles per consumer wave (D / 2 columns)
   constexpr int TT = kSB / 16;         // token tiles
-  constexpr int JPW = 5;               // producer jobs per wave
   using I = Inputs<D, 1>;
   __shared__ SmemWS<D> sm;
 
@@ -827,32 +822,75 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
       const int t0 = sb * kSB;
       const int nt = min(kSB, p.T - t0);
       const int gb = sb & 1;           // gate buffer of this sub-block
-      // K S and Q S of the sub-block's starting state (state as three bf16 pieces)
-      v4f KS[CT][TT], QS[CT][TT];
+      // K S and Q S of the sub-block's starting state (state as three bf16 pieces), and
+      // this wave's query-key tiles Q K^T, whose operands are the same key and query tiles
+      // (lane (l16, qd) holds row l16 of a tile, keys 32 kb + 4 qd + (0..3) and
+      // 32 kb + 16 + 4 qd + (0..3): as the A operand a query row, as the B operand a key
+      // row, in one key order)
+      static_assert(CT == 1, "one column tile per consumer wave");
+      v4f KS[CT][TT], QS[CT][TT], qk[3];
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
+      for (int tt = 0; tt < TT; ++tt) KS[0][tt] = QS[0][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) KS[c][tt] = QS[c][tt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
+      for (int jj = 0; jj < 3; ++jj) qk[jj] = v4f{0.f, 0.f, 0.f, 0.f};
+      // (per wave a compile-time job list: each query-key job is issued as soon as its
+      // query tile is loaded, so only the key tiles it still needs stay in registers)
+      auto ks_qs = [&](auto cwc) {
+        constexpr int CW = decltype(cwc)::value;
 #pragma unroll
         for (int kb = 0; kb < KT / 2; ++kb) {
-          const v4f s0 = S[c][2 * kb], s1 = S[c][2 * kb + 1];
+          const v4f s0 = S[0][2 * kb], s1 = S[0][2 * kb + 1];
           v8bf p0, p1, p2;
           split3(v8f{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]}, p0, p1, p2);
+          v8bf akt[TT];
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) {
             const int row = 16 * tt + l16;
-            const v8bf ak = load_2x4(&sm.K[gb][row][32 * kb + 4 * qd], &sm.K[gb][row][32 * kb + 16 + 4 * qd]);
+            akt[tt] = load_2x4(&sm.K[gb][row][32 * kb + 4 * qd], &sm.K[gb][row][32 * kb + 16 + 4 * qd]);
             const v8bf aq = load_2x4(&sm.Q[row][32 * kb + 4 * qd], &sm.Q[row][32 * kb + 16 + 4 * qd]);
-            KS[c][tt] = mfma_bf16(ak, p0, KS[c][tt]);
-            KS[c][tt] = mfma_bf16(ak, p1, KS[c][tt]);
-            KS[c][tt] = mfma_bf16(ak, p2, KS[c][tt]);
-            QS[c][tt] = mfma_bf16(aq, p0, QS[c][tt]);
-            QS[c][tt] = mfma_bf16(aq, p1, QS[c][tt]);
-            QS[c][tt] = mfma_bf16(aq, p2, QS[c][tt]);
+            KS[0][tt] = mfma_bf16(akt[tt], p0, KS[0][tt]);
+            KS[0][tt] = mfma_bf16(akt[tt], p1, KS[0][tt]);
+            KS[0][tt] = mfma_bf16(akt[tt], p2, KS[0][tt]);
+            QS[0][tt] = mfma_bf16(aq, p0, QS[0][tt]);
+            QS[0][tt] = mfma_bf16(aq, p1, QS[0][tt]);
+            QS[0][tt] = mfma_bf16(aq, p2, QS[0][tt]);
+#pragma unroll
+            for (int jj = 0; jj < kQkCount[CW]; ++jj)
+              if (kQkJobs[CW][jj][0] == tt) qk[jj] = mfma_bf16(aq, akt[kQkJobs[CW][jj][1]], qk[jj]);
           }
         }
+      };
+      switch (wave) {
+        case 0: ks_qs(std::integral_constant<int, 0>{}); break;
+        case 1: ks_qs(std::integral_constant<int, 1>{}); break;
+        case 2: ks_qs(std::integral_constant<int, 2>{}); break;
+        default: ks_qs(std::integral_constant<int, 3>{}); break;
+      }
+      // P = lower-incl [e^{g_t - g_i} q_t . k_i] of this wave's tiles
+      auto qk_epi = [&](auto cwc) {
+        constexpr int CW = decltype(cwc)::value;
+#pragma unroll
+        for (int jj = 0; jj < kQkCount[CW]; ++jj) {
+          const int ti = kQkJobs[CW][jj][0], tj = kQkJobs[CW][jj][1];
+          const float4 g4 = *(const float4*)&sm.g[gb][16 * ti + 4 * qd];
+          const float gi = sm.g[gb][16 * tj + l16];
+          const float gt[4] = {g4.x, g4.y, g4.z, g4.w};
+          const int i = 16 * tj + l16;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * ti + 4 * qd + r;
+            // (the hardware exp2: decays under 2^-126 read as 0, far below any fp32 sum)
+            const float dec = __builtin_amdgcn_exp2f(fminf(gt[r] - gi, 0.f));
+            sm.P[t][i] = t >= i ? dec * qk[jj][r] : 0.f;
+          }
+        }
+      };
+      switch (wave) {
+        case 0: qk_epi(std::integral_constant<int, 0>{}); break;
+        case 1: qk_epi(std::integral_constant<int, 1>{}); break;
+        case 2: qk_epi(std::integral_constant<int, 2>{}); break;
+        default: qk_epi(std::integral_constant<int, 3>{}); break;
+      }
       // right-hand sides R = diag(beta) V - diag(beta Gamma) K S
       v4f R[CT][TT];
       float4 gam4[TT];
@@ -1024,22 +1062,14 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
       const int t0 = sb * kSB;
       const int gb = sb & 1;
       const bool more = sb + 1 < nsb;
-      // ------------------------- Gram and query-key tiles of this sub-block -> A, P
+      // ------------------------------------ Gram tiles of this sub-block -> A
       {
-        v4f acc[JPW];
-        int tis[JPW], tjs[JPW];
-        bool isqs[JPW];
+        v4f acc[3];
 #pragma unroll
-        for (int jj = 0; jj < JPW; ++jj) {
-          const uint32_t code = (ws_job_code(jj) >> (8 * pw)) & 0xFFu;
-          tis[jj] = code & 3;
-          tjs[jj] = (code >> 2) & 3;
-          isqs[jj] = (code >> 4) & 1;
-          acc[jj] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
-        // per 32-key block, the four key tiles and this wave's query tile are each read
-        // once and shared by the five jobs (LDS reads are what the consumers' stage
-        // contends for); the job tiles are compile-time values per wave
+        for (int jj = 0; jj < 3; ++jj) acc[jj] = v4f{0.f, 0.f, 0.f, 0.f};
+        // per 32-key block, the four key tiles are each read once and shared by the jobs
+        // (LDS reads are what the consumers' stage contends for); the job tiles are
+        // compile-time values per wave
         auto gram_mma = [&](auto pwc) {
           constexpr int PW = decltype(pwc)::value;
 #pragma unroll
@@ -1047,11 +1077,27 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
             v8bf kx[TT];
 #pragma unroll
             for (int t = 0; t < TT; ++t) kx[t] = load_8(&sm.K[gb][16 * t + l16][32 * kb + 8 * qd]);
-            const v8bf qx = load_8(&sm.Q[16 * PW + l16][32 * kb + 8 * qd]);
 #pragma unroll
-            for (int jj = 0; jj < JPW; ++jj) {
-              const v8bf xa = kWsJobs[PW][jj][2] ? qx : kx[kWsJobs[PW][jj][0]];
-              acc[jj] = mfma_bf16(xa, kx[kWsJobs[PW][jj][1]], acc[jj]);
+            for (int jj = 0; jj < kKkCount[PW]; ++jj)
+              acc[jj] = mfma_bf16(kx[kKkJobs[PW][jj][0]], kx[kKkJobs[PW][jj][1]], acc[jj]);
+          }
+        };
+        auto gram_epi = [&](auto pwc) {
+          constexpr int PW = decltype(pwc)::value;
+#pragma unroll
+          for (int jj = 0; jj < kKkCount[PW]; ++jj) {
+            const int ti = kKkJobs[PW][jj][0], tj = kKkJobs[PW][jj][1];
+            const float4 g4 = *(const float4*)&sm.g[gb][16 * ti + 4 * qd];
+            const float4 b4 = *(const float4*)&sm.beta[gb][16 * ti + 4 * qd];
+            const float gi = sm.g[gb][16 * tj + l16];
+            const float gt[4] = {g4.x, g4.y, g4.z, g4.w};
+            const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
+            const int i = 16 * tj + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 16 * ti + 4 * qd + r;
+              const float dec = __builtin_amdgcn_exp2f(fminf(gt[r] - gi, 0.f));
+              sm.A[t][i] = t > i ? bt[r] * dec * acc[jj][r] : 0.f;
             }
           }
         };
@@ -1063,27 +1109,11 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(PrefillParams p)
         }
         // the next sub-block's inputs, requested while these tiles are formed
         if (more) load_inputs<D, 1>(in, p, b, h, kh, t0 + kSB, min(kSB, p.T - t0 - kSB), tid);
-        float4 g4[JPW], b4[JPW];
-        float gi[JPW];
-#pragma unroll
-        for (int jj = 0; jj < JPW; ++jj) {
-          g4[jj] = *(const float4*)&sm.g[gb][16 * tis[jj] + 4 * qd];
-          b4[jj] = *(const float4*)&sm.beta[gb][16 * tis[jj] + 4 * qd];
-          gi[jj] = sm.g[gb][16 * tjs[jj] + l16];
-        }
-#pragma unroll
-        for (int jj = 0; jj < JPW; ++jj) {
-          const int i = 16 * tjs[jj] + l16;
-          const float gt[4] = {g4[jj].x, g4[jj].y, g4[jj].z, g4[jj].w};
-          const float bt[4] = {b4[jj].x, b4[jj].y, b4[jj].z, b4[jj].w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * tis[jj] + 4 * qd + r;
-            // (the hardware exp2: decays under 2^-126 read as 0, far below any fp32 sum)
-            const float dec = __builtin_amdgcn_exp2f(fminf(gt[r] - gi[jj], 0.f));
-            if (isqs[jj]) sm.P[t][i] = t >= i ? dec * acc[jj][r] : 0.f;
-            else sm.A[t][i] = t > i ? bt[r] * dec * acc[jj][r] : 0.f;
-          }
+        switch (pw) {
+          case 0: gram_epi(std::integral_constant<int, 0>{}); break;
+          case 1: gram_epi(std::integral_constant<int, 1>{}); break;
+          case 2: gram_epi(std::integral_constant<int, 2>{}); break;
+          default: gram_epi(std::integral_constant<int, 3>{}); break;
         }
       }
       // ---- inverse of diagonal block pw, written above by this wave (its job 0): a
