@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "pace_internal.h"
+#include "pace_lanes.h"
 #include "pace_numerics.h"
 
 namespace pace {
@@ -127,11 +128,6 @@ __device__ inline float row_max16(float x) {
   x = fmaxf(x, dpp<0x141>(x));
   x = fmaxf(x, dpp<0x140>(x));
   return x;
-}
-
-// x of lane (addr / 4), addr precomputed once per thread.
-__device__ inline float lane_read(int addr, float x) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
 }
 
 // Sum of the 8 signed bytes of v.
@@ -708,8 +704,6 @@ void decode_kernel(DecodeParams p) {
 
   // ----------------------------------------- flush: fold on MFMA, requantise
   const float gn = sm.gamma_n;
-  const int ax16 = (lane ^ 16) << 2, ax32 = (lane ^ 32) << 2;   // lanes of the other quarters
-  const int qaddr = l16 << 2;                                       // lane (0, l16); + 64 g: (g, l16)
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     const int c = (wave + kWaves * s) * 16 + l16;    // this lane's column
@@ -777,8 +771,8 @@ void decode_kernel(DecodeParams p) {
             mn = fminf(fminf(mn, acc[2 * kb][i]), acc[2 * kb + 1][i]);
           }
         }
-        mx = fmaxf(mx, lane_read(ax16, mx)); mx = fmaxf(mx, lane_read(ax32, mx));
-        mn = fminf(mn, lane_read(ax16, mn)); mn = fminf(mn, lane_read(ax32, mn));
+        mx = rows_max(mx);
+        mn = rows_min(mn);
       } else {                    // symmetric: only max |x| matters
         mx = 0.f;
 #pragma unroll
@@ -787,7 +781,7 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(fmaxf(mx, fabsf(acc[2 * kb][i])), fabsf(acc[2 * kb + 1][i]));
         }
-        mx = fmaxf(mx, lane_read(ax16, mx)); mx = fmaxf(mx, lane_read(ax32, mx));
+        mx = rows_max(mx);
         mn = -mx;
       }
       gmx[g] = mx;
@@ -803,13 +797,15 @@ void decode_kernel(DecodeParams p) {
     const GroupQuant gq = group_quant(mnm, mxm, asym, bits);
     float rg[4];
     int zg[4];
+    {                                       // the quantiser of group g from row g
+      uint32_t ru[4], zu[4] = {0, 0, 0, 0};
+      rows_gather(f32_bits(gq.r), NG, ru);
+      if (asym) rows_gather((uint32_t)gq.z, NG, zu);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {           // the quantiser of group g from lane (g, l16)
-      rg[g] = 0.f;
-      zg[g] = 0;
-      if (g >= NG) break;
-      rg[g] = lane_read(qaddr + 64 * g, gq.r);
-      if (asym) zg[g] = __builtin_amdgcn_ds_bpermute(qaddr + 64 * g, gq.z);
+      for (int g = 0; g < 4; ++g) {
+        rg[g] = bits_f32(ru[g]);
+        zg[g] = (int)zu[g];
+      }
     }
     if (qq < NG) {
       st_state<NTS>(&g_scales[c * NG + qq], (uint16_t)(f32_bits(gq.s) >> 16));

@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "pace_internal.h"
+#include "pace_lanes.h"
 #include "pace_numerics.h"
 
 namespace pace {
@@ -71,7 +72,7 @@ template <int D>
 __device__ inline void store_codes4(const Rec& r, int j, int kt, int qd, uint32_t c4) {
   uint8_t* up = unit_ptr<D>(r, j, 2 * kt + (qd >> 1));
   if (r.bits == 4) {
-    const uint32_t hi = __shfl_xor(c4, 16);          // keys 8m + 4 .. 8m + 7 (lane group qd ^ 1)
+    const uint32_t hi = pair16(c4).hi;               // keys 8m + 4 .. 8m + 7 (lane group qd | 1)
     if ((qd & 1) == 0) *(uint32_t*)up = c4 | (hi << 4);
   } else {
     *(uint32_t*)(up + 4 * (qd & 1)) = c4;
@@ -92,8 +93,8 @@ __device__ inline void requant_tile(v4f (&S)[D / 16], const Rec& r, int j, int q
     for (int kk = 0; kk < KPG; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i) { mx = fmaxf(mx, S[G * KPG + kk][i]); mn = fminf(mn, S[G * KPG + kk][i]); }
-    mx = fmaxf(mx, __shfl_xor(mx, 16)); mn = fminf(mn, __shfl_xor(mn, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)); mn = fminf(mn, __shfl_xor(mn, 32));
+    mx = rows_max(mx);
+    mn = rows_min(mn);
     const GroupQuant gq = group_quant(mn, mx, r.asym != 0, r.bits);
     const CodeRange cr = code_range(gq.z, r.asym != 0, r.bits);
     const float fz = (float)gq.z;
