@@ -55,6 +55,14 @@ CASES = {
     # mixed buffer
     "asym_g64_int8": (2, 8, 4, 128, 64, True, "int8", True, 8, [4, 8, 4, 4, 8, 4, 4, 4]),
     "sym4_g64_mixed": (2, 8, 4, 128, 64, False, "mixed", True, 8, None),
+    # asymmetric 32-key groups with every head at 4 bits (no 8-bit heads)
+    "asym_g32_4bit_int8": (2, 8, 4, 128, 32, True, "int8", True, 8, None),
+    # general kernels: fp32 I/O at d = 128 (both buffers), a 32-slot buffer at d = 128, the
+    # mixed buffer with bf16 I/O at d = 64
+    "d128_f32_sym_g64_mixed": (2, 4, 2, 128, 64, False, "mixed", False, 8, None),
+    "d128_f32_asym_g32_int8": (2, 4, 2, 128, 32, True, "int8", False, 8, None),
+    "d128_dP12_asym_int8": (2, 4, 2, 128, 32, True, "int8", True, 12, [4, 8, 4, 4]),
+    "d64_bf16_asym_mixed": (2, 4, 2, 64, 32, True, "mixed", True, 8, [8, 4, 4, 4]),
 }
 
 
@@ -210,7 +218,8 @@ def test_decode_inactive_sequences_untouched():
     check_states(ocfg, s_gpu, state, pre, [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)], "active")
 
 
-@pytest.mark.parametrize("name", ["pace4_g64_int8", "pace48_g32_mixed", "d64_asym_mixed_f32", "asym_g64_int8"])
+@pytest.mark.parametrize("name", ["pace4_g64_int8", "pace48_g32_mixed", "d64_asym_mixed_f32", "asym_g64_int8",
+                                  "d128_f32_asym_g32_int8"])
 def test_flush_requant_matches_oracle(name):
     print(f"[flush parity] case={name}", flush=True)
     ocfg, gcfg, state, buffer, _ = make_case(name, seed=300 + len(name))

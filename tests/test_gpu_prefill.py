@@ -26,9 +26,14 @@ def _lib():
 
 PCASES = {
     # name: (B, Hv, Hk, d, group, asym, bf16, head_bits)
+    # d = 64 (fp32 / bf16 I/O): one four-wave workgroup per (sequence, head)
     "tiny_sym4_g32_f32": (2, 4, 4, 64, 32, False, False, None),
+    "d64_asym_g32_bf16": (2, 4, 2, 64, 32, True, True, [4, 8, 4, 4]),
+    # d = 128, bf16 I/O: the warp-specialised kernel, two column blocks per pair
     "pace4_g64_bf16": (2, 32, 16, 128, 64, False, True, None),
     "pace48_g32_bf16": (2, 8, 4, 128, 32, True, True, [8, 4, 4, 4, 4, 8, 4, 4]),
+    # d = 128, fp32 I/O, few pairs: the four-wave kernel with the columns split in two
+    "d128_sym_g64_f32": (2, 8, 4, 128, 64, False, False, None),
 }
 
 
@@ -124,18 +129,20 @@ def test_prefill_long_shape_first_chunk_sampled():
     check_prefill_call(ocfg, gcfg, zero, toks.span(0, 256), tiles, "long/first-chunk")
 
 
-def test_prefill_many_pairs_one_block_per_pair():
-    """512 (sequence, head) pairs at d = 128: one workgroup per pair owns all value columns
-    (fewer pairs split each one over two column blocks, as every test above does); a
-    partial chunk, sampled tiles against the oracle."""
-    print("[prefill parity] 512 pairs, whole-column workgroups", flush=True)
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "f32"])
+def test_prefill_many_pairs(bf16):
+    """512 (sequence, head) pairs at d = 128, a partial chunk, sampled tiles against the
+    oracle.  bf16: the warp-specialised kernel's 1,024 workgroups take more than one round
+    of the CUs; fp32: twice the pairs no longer fit the CUs, so one workgroup per pair owns
+    all value columns."""
+    print(f"[prefill parity] 512 pairs, bf16={bf16}", flush=True)
     B, Hv, Hk, d = 16, 32, 16, 128
-    ocfg = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, asym=False, buf="int8", dP=8, bf16_io=True)
-    gcfg = _lib().LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, bf16_io=True)
-    toks = make_tokens(16, B, 96, Hv, Hk, d, d, bf16=True)
+    ocfg = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, asym=False, buf="int8", dP=8, bf16_io=bf16)
+    gcfg = _lib().LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, bf16_io=bf16)
+    toks = make_tokens(16, B, 96, Hv, Hk, d, d, bf16=bf16)
     zero = np.zeros(pk.state_layout(ocfg)[2], dtype=np.uint8)
     tiles = [(0, 0), (3, 9), (7, 16), (15, 31)]
-    check_prefill_call(ocfg, gcfg, zero, toks.span(0, 96), tiles, "512pairs/partial")
+    check_prefill_call(ocfg, gcfg, zero, toks.span(0, 96), tiles, f"512pairs/partial/bf16={bf16}")
 
 
 def test_long_prefill_full_size():
