@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--staggered", action="store_true", default=True)
+    ap.add_argument("--no-staggered", dest="staggered", action="store_false")
     ap.add_argument("--sweep", action="store_true", default=True)
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
     ap.add_argument("--sweep-batches", default="1,16,32,64,128")
@@ -253,19 +255,40 @@ def build_layers(torch, pace, args, cfgs):
     return layers, L
 
 
-def run_decode(torch, pace, args, B, steps, warmup, split=False):
-    """Decode periods of the L-layer stack at batch B.  Returns a dict of figures."""
+def run_decode(torch, pace, args, B, steps, warmup, split=False, phases=None, ordered=False):
+    """Decode periods of the L-layer stack at batch B.  Returns a dict of figures.
+
+    phases: optional per-sequence buffer counts to start from (continuous batching:
+    sequences that joined at different times flush at different steps).  They are set
+    by decode steps under the active mask before timing; every sequence still passes
+    through each count once per period, so the bytes and tokens of a period are those
+    of the aligned case.  ordered: issue each step through pace_decode_step_ordered with
+    the sequences that flush at that step placed first (what a continuous-batching
+    scheduler, which knows every sequence's position in its period, would pass)."""
     t0 = time.time()
     cfgs = make_cfgs(torch, pace, args, B)
     cfg = cfgs[0]
     dP, Lyr = cfg.dP, args.layers
     layers, L = build_layers(torch, pace, args, cfgs)
+    if phases is not None:
+        ph = np.asarray(phases)
+        for k in range(1, dP):
+            mask = torch.from_numpy((ph >= k).astype(np.uint8)).cuda()
+            for ly in layers:
+                q, k_, v, a, b_ = ly["toks"][k - 1]
+                pace.decode_step(ly["cfg"], ly["state"], ly["buf"], q, k_, v, a, b_, ly["o"], active=mask)
+        torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     calls = []
     for t in range(dP):
+        order = None
+        if ordered and phases is not None:
+            flushing = (np.asarray(phases) + t) % dP == dP - 1
+            order = np.concatenate([np.flatnonzero(flushing), np.flatnonzero(~flushing)])
         for ly in layers:
             q, k, v, a, b_ = ly["toks"][t]
-            calls.append(pace.prepare_decode_step(ly["cfg"], ly["state"], ly["buf"], q, k, v, a, b_, ly["o"], stream=stream))
+            calls.append(pace.prepare_decode_step(ly["cfg"], ly["state"], ly["buf"], q, k, v, a, b_, ly["o"],
+                                                  stream=stream, order=order))
     ms = time_graph(torch, stream, calls, steps, warmup)
     n_launch = len(calls) * steps
     launch_s = ms / 1e3 / n_launch                       # mean launch duration in the timed region
@@ -464,6 +487,25 @@ def main():
         result["bf16_baseline"] = run_bf16_baseline(torch, pace, args, cfg, layers)
     del layers
     torch.cuda.empty_cache()
+
+    # ---- continuous batching: the same stack with every sequence at its own point of
+    # the period (seeded uniform phases), so each step flushes about 1/dP of the tiles
+    if args.staggered:
+        phases = np.random.default_rng(args.seed + 17).integers(0, dP, size=B)
+        stag = {"workload": "as config, each sequence starting at a seeded uniform random position of its "
+                            f"{dP}-token period (flushes spread over the steps)"}
+        for key, ordered in (("sequence_order", True), ("launch_order", False)):
+            rs = run_decode(torch, pace, args, B, args.steps, args.warmup, phases=phases, ordered=ordered)
+            stag[key] = {"tokens_per_s": round(rs["tokens_per_s"], 1), "ms_per_step": round(rs["ms_per_step"], 4),
+                         "mean_launch_us": round(rs["launch_us"], 3), "GBps": round(rs["achieved"], 1),
+                         "frac": round(rs["achieved"] / HBM_PEAK_GBS, 4),
+                         "vs_aligned": round(rs["tokens_per_s"] / r["tokens_per_s"], 4)}
+            del rs["layers"]
+            torch.cuda.empty_cache()
+        stag["note"] = ("sequence_order: pace_decode_step_ordered with the sequences that flush at each step "
+                        "placed first; launch_order: pace_decode_step (sequence b on workgroup row b)")
+        result["staggered_phases"] = stag
+        log(f"staggered phases: {stag}")
 
     # ---- batch sweep (PACE-4 and the bf16 baseline at each B)
     if args.sweep:

@@ -11,6 +11,8 @@ import os
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
+import numpy as np
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpace.so")
 
@@ -42,8 +44,8 @@ class _Info(ctypes.Structure):
 
 
 EXPORTS = ["pace_layout", "pace_head_alloc", "pace_calibrate_heads", "pace_prefill_chunk",
-           "pace_prefill_workspace_bytes", "pace_decode_step", "pace_flush_requant",
-           "pace_bf16_decode_step", "pace_status_str"]
+           "pace_prefill_workspace_bytes", "pace_decode_step", "pace_decode_step_ordered",
+           "pace_flush_requant", "pace_bf16_decode_step", "pace_status_str"]
 
 
 def _load():
@@ -60,13 +62,14 @@ def _load():
     lib.pace_prefill_workspace_bytes.argtypes = [C, ctypes.c_int32]
     lib.pace_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.pace_decode_step.argtypes = [C, P, P, P, P, P, P, P, P, P, P]
+    lib.pace_decode_step_ordered.argtypes = [C, P, P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_int32), P, P]
     lib.pace_flush_requant.argtypes = [C, P, P, P, P]
     lib.pace_bf16_decode_step.argtypes = [C, P, P, P, P, P, P, P, P]
     lib.pace_calibrate_heads.argtypes = [C, P, P, P, P, ctypes.c_int32, P, P, P]
     lib.pace_status_str.argtypes = [ctypes.c_int]
     lib.pace_status_str.restype = ctypes.c_char_p
     for name in ["pace_layout", "pace_head_alloc", "pace_prefill_chunk", "pace_decode_step",
-                 "pace_flush_requant", "pace_bf16_decode_step", "pace_calibrate_heads"]:
+                 "pace_decode_step_ordered", "pace_flush_requant", "pace_bf16_decode_step", "pace_calibrate_heads"]:
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -163,22 +166,41 @@ def _io(cfg):
     return torch.bfloat16 if cfg.bf16_io else torch.float32
 
 
-def decode_step(cfg: LayerConfig, state, buffer, q, k, v, a, beta, o, active=None, stream=None):
-    """pace_decode_step.  q, k [B, Hk, dk]; v, o [B, Hv, dv]; a, beta fp32 [B, Hv];
-    state / buffer uint8 tensors of pace_layout sizes; active optional uint8 [B]."""
+def _order(cfg: LayerConfig, order):
+    """Host int32 copy of a sequence order (pace_decode_step_ordered checks it)."""
+    arr = np.ascontiguousarray(np.asarray(order, dtype=np.int32))
+    if arr.shape != (cfg.B,):
+        raise ValueError(f"order: expected {cfg.B} sequence indices, got shape {arr.shape}")
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _decode_args(cfg: LayerConfig, state, buffer, q, k, v, a, beta, o, active, stream, order):
+    """(function, name, marshalled arguments, objects to keep alive) of one decode step."""
     import torch
     L = layout(cfg)
     io = _io(cfg)
     c = cfg._c()
-    st = LIB.pace_decode_step(
-        ctypes.byref(c), _ptr(state, "state", torch.uint8, L["state_bytes"]),
-        _ptr(buffer, "buffer", torch.uint8, L["buffer_bytes"]),
-        _ptr(q, "q", io, cfg.B * cfg.Hk * cfg.dk), _ptr(k, "k", io, cfg.B * cfg.Hk * cfg.dk),
-        _ptr(v, "v", io, cfg.B * cfg.Hv * cfg.dv), _ptr(a, "a", torch.float32, cfg.B * cfg.Hv),
-        _ptr(beta, "beta", torch.float32, cfg.B * cfg.Hv),
-        _ptr(active, "active", torch.uint8, cfg.B, optional=True),
-        _ptr(o, "o", io, cfg.B * cfg.Hv * cfg.dv), _stream(stream))
-    _check(st, "pace_decode_step")
+    head = (ctypes.byref(c), _ptr(state, "state", torch.uint8, L["state_bytes"]),
+            _ptr(buffer, "buffer", torch.uint8, L["buffer_bytes"]),
+            _ptr(q, "q", io, cfg.B * cfg.Hk * cfg.dk), _ptr(k, "k", io, cfg.B * cfg.Hk * cfg.dk),
+            _ptr(v, "v", io, cfg.B * cfg.Hv * cfg.dv), _ptr(a, "a", torch.float32, cfg.B * cfg.Hv),
+            _ptr(beta, "beta", torch.float32, cfg.B * cfg.Hv),
+            _ptr(active, "active", torch.uint8, cfg.B, optional=True))
+    tail = (_ptr(o, "o", io, cfg.B * cfg.Hv * cfg.dv), _stream(stream))
+    if order is None:
+        return LIB.pace_decode_step, "pace_decode_step", head + tail, (c,)
+    arr, ptr = _order(cfg, order)
+    return LIB.pace_decode_step_ordered, "pace_decode_step_ordered", head + (ptr,) + tail, (c, arr)
+
+
+def decode_step(cfg: LayerConfig, state, buffer, q, k, v, a, beta, o, active=None, stream=None,
+                order=None):
+    """pace_decode_step (pace_decode_step_ordered when `order` is given: a host sequence
+    of the B sequence indices, the sequences to start first listed first).  q, k
+    [B, Hk, dk]; v, o [B, Hv, dv]; a, beta fp32 [B, Hv]; state / buffer uint8 tensors of
+    pace_layout sizes; active optional uint8 [B]."""
+    fn, name, args, _keep = _decode_args(cfg, state, buffer, q, k, v, a, beta, o, active, stream, order)
+    _check(fn(*args), name)
 
 
 def flush_requant(cfg: LayerConfig, state, buffer, seq_mask=None, stream=None):
@@ -272,28 +294,19 @@ def bf16_decode_step(cfg: LayerConfig, state, q, k, v, a, beta, o, stream=None):
     _check(st, "pace_bf16_decode_step")
 
 
-def prepare_decode_step(cfg: LayerConfig, state, buffer, q, k, v, a, beta, o, active=None, stream=None):
-    """Validate and marshal the arguments of pace_decode_step once; returns a callable
-    that issues the same call again with no Python-side checks (for graph capture and
-    timing loops).  The tensors must stay alive while the callable is used."""
-    import torch
-    L = layout(cfg)
-    io = _io(cfg)
-    c = cfg._c()
-    args = (ctypes.byref(c), _ptr(state, "state", torch.uint8, L["state_bytes"]),
-            _ptr(buffer, "buffer", torch.uint8, L["buffer_bytes"]),
-            _ptr(q, "q", io, cfg.B * cfg.Hk * cfg.dk), _ptr(k, "k", io, cfg.B * cfg.Hk * cfg.dk),
-            _ptr(v, "v", io, cfg.B * cfg.Hv * cfg.dv), _ptr(a, "a", torch.float32, cfg.B * cfg.Hv),
-            _ptr(beta, "beta", torch.float32, cfg.B * cfg.Hv),
-            _ptr(active, "active", torch.uint8, cfg.B, optional=True),
-            _ptr(o, "o", io, cfg.B * cfg.Hv * cfg.dv), _stream(stream))
-    fn = LIB.pace_decode_step
+def prepare_decode_step(cfg: LayerConfig, state, buffer, q, k, v, a, beta, o, active=None, stream=None,
+                        order=None):
+    """Validate and marshal the arguments of pace_decode_step (or, with `order`,
+    pace_decode_step_ordered) once; returns a callable that issues the same call again
+    with no Python-side checks (for graph capture and timing loops).  The tensors must
+    stay alive while the callable is used."""
+    fn, name, args, keep = _decode_args(cfg, state, buffer, q, k, v, a, beta, o, active, stream, order)
 
     def call():
         st = fn(*args)
         if st != PACE_OK:
-            raise PaceError(st, "pace_decode_step")
-    call._keep = (c, args)
+            raise PaceError(st, name)
+    call._keep = (keep, args)
     return call
 
 

@@ -171,11 +171,19 @@ struct alignas(16) Smem {
 // GT: scale-group size (32 or 64), 0 = taken from the parameters at run time.
 // AS: 0 = symmetric, 1 = asymmetric, 2 = taken from the parameters at run time.
 // NTS: the state's codes, scales and zero points are read and written non-temporally.
-template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS>
+// Second kernel argument: the sequence order of ordered launches, nothing otherwise (so
+// that launches in plain order keep their argument block and their first addresses need
+// no extra load).
+template <bool ORD>
+struct OrderArg : SeqOrder {};
+template <>
+struct OrderArg<false> {};
+
+template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS, bool ORD = false>
 // Eight resident workgroups per CU (four waves per SIMD) for the specialised dP <= 8
 // variants, so a 2048-tile launch runs in one round: at most 128 VGPRs.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOK <= 8 && GT != 0 ? 4 : 1)))
-void decode_kernel(DecodeParams p) {
+void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
   using SM = Smem<D, TOK>;
   constexpr int NV = SM::NV;
   constexpr int NT = NV / 16;           // 16-vector MFMA column tiles
@@ -195,7 +203,10 @@ void decode_kernel(DecodeParams p) {
   // XCDs in turn by linear id, so within each block of 8 gamma heads the heads of one key
   // head are placed 8 ids apart (power-of-two gamma, Hv a multiple of 8 gamma).
   int h = blockIdx.x;
-  const int b = blockIdx.y;
+  // the sequence of this workgroup row: the caller's order (validated as a permutation on
+  // the host) in ordered launches
+  int b = blockIdx.y;
+  if constexpr (ORD) b = ord.seq[blockIdx.y];
   if (p.gamma > 1 && (p.gamma & (p.gamma - 1)) == 0 && p.Hv % (8 * p.gamma) == 0) {
     const int lg = __builtin_ctz(p.gamma);
     const int r = h & (8 * p.gamma - 1);
@@ -868,9 +879,12 @@ void decode_kernel(DecodeParams p) {
   if (tid == 0) *countp = 0;
 }
 
-template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS = false>
-hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, TOK, BUF, HB, IO, GT, AS, NTS>), dim3((unsigned)p.Hv, (unsigned)p.B), dim3(kThreads), 0, stream, p);
+template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS = false, bool ORD = false>
+hipError_t launch_t(const DecodeParams& p, const SeqOrder* order, hipStream_t stream) {
+  OrderArg<ORD> ord{};
+  if constexpr (ORD) static_cast<SeqOrder&>(ord) = *order;
+  hipLaunchKernelGGL((decode_kernel<D, TOK, BUF, HB, IO, GT, AS, NTS, ORD>), dim3((unsigned)p.Hv, (unsigned)p.B),
+                     dim3(kThreads), 0, stream, p, ord);
   return hipGetLastError();
 }
 
@@ -883,38 +897,47 @@ constexpr uint64_t kStreamStateBytes = 8ull << 20;
 
 // Specialised instantiations for the layouts the method names (d = 128, dP <= 8, bf16
 // I/O; 64-key symmetric and 32-key asymmetric groups, and their mirror images), with
-// group size and symmetry known at compile time.
-template <int BUF, int HB, bool NT>
-hipError_t launch_fast_nt(const DecodeParams& p, hipStream_t stream) {
-  if (p.group == 64) return p.asym ? launch_t<128, 8, BUF, HB, 1, 64, 1, NT>(p, stream) : launch_t<128, 8, BUF, HB, 1, 64, 0, NT>(p, stream);
-  return p.asym ? launch_t<128, 8, BUF, HB, 1, 32, 1, NT>(p, stream) : launch_t<128, 8, BUF, HB, 1, 32, 0, NT>(p, stream);
+// group size and symmetry known at compile time; in launch order or in a given order.
+template <int BUF, int HB, bool NT, bool ORD>
+hipError_t launch_fast_nt(const DecodeParams& p, const SeqOrder* o, hipStream_t stream) {
+  if (p.group == 64)
+    return p.asym ? launch_t<128, 8, BUF, HB, 1, 64, 1, NT, ORD>(p, o, stream)
+                  : launch_t<128, 8, BUF, HB, 1, 64, 0, NT, ORD>(p, o, stream);
+  return p.asym ? launch_t<128, 8, BUF, HB, 1, 32, 1, NT, ORD>(p, o, stream)
+                : launch_t<128, 8, BUF, HB, 1, 32, 0, NT, ORD>(p, o, stream);
+}
+template <int BUF, int HB, bool ORD>
+hipError_t launch_fast_o(const DecodeParams& p, const SeqOrder* o, hipStream_t stream) {
+  const bool stream_state = (uint64_t)p.B * p.seq_stride >= kStreamStateBytes;
+  return stream_state ? launch_fast_nt<BUF, HB, true, ORD>(p, o, stream)
+                      : launch_fast_nt<BUF, HB, false, ORD>(p, o, stream);
 }
 template <int BUF, int HB>
-hipError_t launch_fast(const DecodeParams& p, hipStream_t stream) {
-  const bool stream_state = (uint64_t)p.B * p.seq_stride >= kStreamStateBytes;
-  return stream_state ? launch_fast_nt<BUF, HB, true>(p, stream) : launch_fast_nt<BUF, HB, false>(p, stream);
+hipError_t launch_fast(const DecodeParams& p, const SeqOrder* o, hipStream_t stream) {
+  return o ? launch_fast_o<BUF, HB, true>(p, o, stream) : launch_fast_o<BUF, HB, false>(p, nullptr, stream);
 }
 
 template <int D, int BUF, int IO>
 hipError_t launch_generic(const DecodeParams& p, hipStream_t stream) {
-  if (p.dP <= 8) return launch_t<D, 8, BUF, 0, IO, 0, 2>(p, stream);
-  return launch_t<D, 32, BUF, 0, IO, 0, 2>(p, stream);
+  if (p.dP <= 8) return launch_t<D, 8, BUF, 0, IO, 0, 2>(p, nullptr, stream);
+  return launch_t<D, 32, BUF, 0, IO, 0, 2>(p, nullptr, stream);
 }
 
 template <int BUF>
-hipError_t launch_buf(const DecodeParams& p, int dk, hipStream_t stream) {
+hipError_t launch_buf(const DecodeParams& p, const SeqOrder* o, int dk, hipStream_t stream) {
   if (dk == 128 && p.dP <= 8 && p.io_bf16)
-    return p.mask8 == 0 ? launch_fast<BUF, 4>(p, stream) : launch_fast<BUF, 0>(p, stream);
+    return p.mask8 == 0 ? launch_fast<BUF, 4>(p, o, stream) : launch_fast<BUF, 0>(p, o, stream);
   if (dk == 128) return p.io_bf16 ? launch_generic<128, BUF, 1>(p, stream) : launch_generic<128, BUF, 0>(p, stream);
   return p.io_bf16 ? launch_generic<64, BUF, 1>(p, stream) : launch_generic<64, BUF, 0>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int dk, int dv, int buf_kind, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, const SeqOrder* order, int dk, int dv, int buf_kind,
+                         hipStream_t stream) {
   (void)dv;  // dk == dv is validated by the caller
-  if (buf_kind == PACE_BUF_INT8) return launch_buf<PACE_BUF_INT8>(p, dk, stream);
-  return launch_buf<PACE_BUF_K4_VBF16>(p, dk, stream);
+  if (buf_kind == PACE_BUF_INT8) return launch_buf<PACE_BUF_INT8>(p, order, dk, stream);
+  return launch_buf<PACE_BUF_K4_VBF16>(p, order, dk, stream);
 }
 
 }  // namespace pace

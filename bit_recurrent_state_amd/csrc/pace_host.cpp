@@ -129,10 +129,11 @@ size_t pace_prefill_workspace_bytes(const pace_layer_cfg* cfg, int32_t T) {
   return prefill_workspace_bytes(cfg->B, cfg->Hv, cfg->dk, cfg->dv, T, cfg->chunk);
 }
 
-pace_status pace_decode_step(const pace_layer_cfg* cfg, void* state, void* buffer,
-                             const void* q, const void* k, const void* v, const float* a,
-                             const float* beta, const uint8_t* active, void* o,
-                             void* stream) {
+namespace {
+
+pace_status decode_step(const pace_layer_cfg* cfg, void* state, void* buffer, const void* q,
+                        const void* k, const void* v, const float* a, const float* beta,
+                        const uint8_t* active, const int32_t* seq_order, void* o, void* stream) {
   const pace_status st = validate(cfg);
   if (st != PACE_OK) return st;
   if (!state || !buffer || !q || !k || !v || !a || !beta || !o) return PACE_EINVAL;
@@ -158,8 +159,38 @@ pace_status pace_decode_step(const pace_layer_cfg* cfg, void* state, void* buffe
   p.dP = cfg->dP; p.group = cfg->group; p.asym = cfg->state_kind == PACE_STATE_ASYM;
   p.flush_only = 0;
   p.io_bf16 = cfg->io_dtype == PACE_IO_BF16;
-  const hipError_t e = launch_decode(p, cfg->dk, cfg->dv, cfg->buf_kind, (hipStream_t)stream);
+  SeqOrder order{};
+  if (seq_order) {
+    // a permutation of 0..B-1, checked here so that the kernel can trust it
+    if (cfg->B > kMaxOrderedBatch) return PACE_EUNSUPPORTED;
+    uint8_t seen[kMaxOrderedBatch] = {};
+    for (int y = 0; y < cfg->B; ++y) {
+      const int32_t sb = seq_order[y];
+      if (sb < 0 || sb >= cfg->B || seen[sb]) return PACE_EINVAL;
+      seen[sb] = 1;
+      order.seq[y] = (uint8_t)sb;
+    }
+  }
+  const hipError_t e = launch_decode(p, seq_order ? &order : nullptr, cfg->dk, cfg->dv, cfg->buf_kind,
+                                     (hipStream_t)stream);
   return e == hipSuccess ? PACE_OK : PACE_EHIP;
+}
+
+}  // namespace
+
+pace_status pace_decode_step(const pace_layer_cfg* cfg, void* state, void* buffer,
+                             const void* q, const void* k, const void* v, const float* a,
+                             const float* beta, const uint8_t* active, void* o,
+                             void* stream) {
+  return decode_step(cfg, state, buffer, q, k, v, a, beta, active, nullptr, o, stream);
+}
+
+pace_status pace_decode_step_ordered(const pace_layer_cfg* cfg, void* state, void* buffer,
+                                     const void* q, const void* k, const void* v, const float* a,
+                                     const float* beta, const uint8_t* active,
+                                     const int32_t* seq_order, void* o, void* stream) {
+  if (!seq_order) return PACE_EINVAL;
+  return decode_step(cfg, state, buffer, q, k, v, a, beta, active, seq_order, o, stream);
 }
 
 pace_status pace_flush_requant(const pace_layer_cfg* cfg, void* state, void* buffer,
@@ -190,7 +221,7 @@ pace_status pace_flush_requant(const pace_layer_cfg* cfg, void* state, void* buf
   // use the values
   p.q = p.k = p.v = state;
   p.a = p.beta = (const float*)state;
-  const hipError_t e = launch_decode(p, cfg->dk, cfg->dv, cfg->buf_kind, (hipStream_t)stream);
+  const hipError_t e = launch_decode(p, nullptr, cfg->dk, cfg->dv, cfg->buf_kind, (hipStream_t)stream);
   return e == hipSuccess ? PACE_OK : PACE_EHIP;
 }
 

@@ -13,6 +13,7 @@ namespace pace {
 
 constexpr int kMaxHeads = 64;    // head bit map is a 64-bit mask
 constexpr int kMaxPeriod = 32;   // decode period dP upper bound
+constexpr int kMaxOrderedBatch = 256;   // batch bound of pace_decode_step_ordered
 
 inline size_t pad_to(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
@@ -80,6 +81,13 @@ struct DecodeParams {
   int32_t io_bf16;      // q, k, v, o are bf16 (else fp32)
 };
 
+// Sequence order of an ordered decode launch, passed by value as a second kernel argument
+// of its own (only the ordered instantiations take it): workgroup row y runs sequence
+// seq[y], a permutation of 0..B-1 checked on the host.
+struct SeqOrder {
+  uint8_t seq[kMaxOrderedBatch];
+};
+
 struct PrefillParams {
   uint8_t* state;
   const void* q;
@@ -118,7 +126,10 @@ struct CalibParams {
 };
 
 // Launchers (defined next to their kernels).  They only enqueue work.
-hipError_t launch_decode(const DecodeParams& p, int dk, int dv, int buf_kind, hipStream_t stream);
+// order: null for launch order; otherwise the specialised kernels place the sequences as
+// it says (the general ones, which it cannot change the results of either, ignore it).
+hipError_t launch_decode(const DecodeParams& p, const SeqOrder* order, int dk, int dv, int buf_kind,
+                         hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dk, int dv, int io_bf16,
                           hipStream_t stream);
 size_t prefill_workspace_bytes(int B, int Hv, int dk, int dv, int T, int chunk);

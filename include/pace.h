@@ -222,6 +222,23 @@ pace_status pace_decode_step(const pace_layer_cfg* cfg, void* state, void* buffe
                              const float* beta, const uint8_t* active, void* o,
                              void* stream);
 
+/* pace_decode_step with a caller-chosen order of the sequences over the launch, for
+ * continuous batching ([p1] "How it works": each serving sequence keeps its own state and
+ * buffer, so sequences that joined at different times flush at different steps).  Results
+ * are those of pace_decode_step, bit for bit: only the placement of the work changes.
+ * seq_order: HOST array of B indices, a permutation of 0..B-1; the sequences listed first
+ * are started first and spread one per compute unit (place those whose buffer holds dP-1
+ * tokens, i.e. that flush at this step, first).  It is copied into the launch, so the
+ * array may be reused at once (and a captured graph keeps the order it was captured with).
+ * The order is applied by the kernels of the layouts the method names (dk = 128,
+ * dP <= 8, bf16 I/O); other configurations run in launch order.
+ * Errors: PACE_EINVAL for a null seq_order or one that is not a permutation of 0..B-1,
+ * PACE_EUNSUPPORTED for B > 256; otherwise as pace_decode_step. */
+pace_status pace_decode_step_ordered(const pace_layer_cfg* cfg, void* state, void* buffer,
+                                     const void* q, const void* k, const void* v, const float* a,
+                                     const float* beta, const uint8_t* active,
+                                     const int32_t* seq_order, void* o, void* stream);
+
 /* Explicit flush (sequence end, eviction, checkpoint): for every sequence with
  * seq_mask[b] != 0 (NULL = all) and 0 < count < dP, fold the buffered tokens into the
  * state, requantise once and set count = 0.  A sequence with count == 0 is untouched. */

@@ -88,7 +88,7 @@ def make_case(name, seed, counts=None):
     return ocfg, gcfg, state, buffer, toks
 
 
-def run_gpu_decode(gcfg, state, buffer, toks, active=None):
+def run_gpu_decode(gcfg, state, buffer, toks, active=None, order=None):
     pace = _lib()
     q, k, v, a, beta = toks.token(0)
     bf16 = gcfg.bf16_io
@@ -98,7 +98,7 @@ def run_gpu_decode(gcfg, state, buffer, toks, active=None):
                    dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
     act = dev(np.asarray(active, dtype=np.uint8)) if active is not None else None
     pace.decode_step(gcfg, st, bu, io_dev(q, bf16), io_dev(k, bf16), io_dev(v, bf16), dev(a), dev(beta), o,
-                     active=act)
+                     active=act, order=order)
     torch.cuda.synchronize()
     return host(o), st.cpu().numpy(), bu.cpu().numpy()
 
@@ -216,6 +216,29 @@ def test_decode_inactive_sequences_untouched():
             assert np.isnan(o_gpu[b]).all(), "inactive output written"
     compare_buffers(ocfg, b_gpu, b_ref, [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)])
     check_states(ocfg, s_gpu, state, pre, [(b, h) for b in range(ocfg.B) for h in range(ocfg.Hv)], "active")
+
+
+@pytest.mark.parametrize("name", ["pace4_g64_int8", "pace48_g32_mixed", "d64_asym_mixed_f32"])
+def test_ordered_decode_equals_unordered(name):
+    """pace_decode_step_ordered (continuous batching: the sequences that flush at this step
+    placed first) gives the results of pace_decode_step bit for bit -- outputs, packed
+    state and buffer -- for a random order, with and without an active mask; the outputs
+    also match the oracle."""
+    print(f"[ordered decode] case={name}", flush=True)
+    ocfg, gcfg, state, buffer, toks = make_case(name, seed=300 + len(name))
+    B = gcfg.B
+    order = np.random.default_rng(5 + B).permutation(B)
+    o_ref, _, _, _ = pk.decode_step_layer(ocfg, state, buffer, *toks.token(0))
+    for active in (None, [1 if b % 3 else 0 for b in range(B)]):
+        o1, s1, b1 = run_gpu_decode(gcfg, state, buffer, toks, active=active)
+        o2, s2, b2 = run_gpu_decode(gcfg, state, buffer, toks, active=active, order=order)
+        both_nan = np.isnan(o1) & np.isnan(o2)          # rows of inactive sequences stay unwritten
+        assert np.array_equal(np.where(both_nan, 0, o1), np.where(both_nan, 0, o2)), "outputs differ"
+        assert np.array_equal(s1, s2), "packed state differs"
+        assert np.array_equal(b1, b2), "buffer differs"
+    tiles = [(b, h) for b in range(B) for h in range(gcfg.Hv)]
+    o2, _, _ = run_gpu_decode(gcfg, state, buffer, toks, order=order)
+    parity.check_outputs(o2, o_ref, tiles, name + "/ordered", out_bf16=ocfg.bf16_io)
 
 
 @pytest.mark.parametrize("name", ["pace4_g64_int8", "pace48_g32_mixed", "d64_asym_mixed_f32", "asym_g64_int8",

@@ -148,3 +148,26 @@ def test_null_pointers_rejected_before_any_launch():
     st = L.LIB.pace_decode_step(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, None, fake, None)
     assert st == pace.PACE_EINVAL
     assert L.LIB.pace_status_str(-2).decode().startswith("PACE_EUNSUPPORTED")
+
+
+def test_sequence_order_validated_before_any_launch():
+    """pace_decode_step_ordered takes a host permutation of the B sequences; anything else
+    is refused on the host (aligned stand-in device pointers, never dereferenced)."""
+    pace = _pace()
+    L = pace._lib
+    fake = ctypes.c_void_p(0x10000)
+
+    def call(B, order):
+        c = pace.LayerConfig(B=B, Hv=4, Hk=4, dk=64, dv=64, group=32)._c()
+        ptr = None if order is None else np.asarray(order, dtype=np.int32).ctypes.data_as(
+            ctypes.POINTER(ctypes.c_int32))
+        return L.LIB.pace_decode_step_ordered(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake,
+                                              None, ptr, fake, None)
+
+    assert call(4, None) == pace.PACE_EINVAL
+    assert call(4, [0, 1, 1, 3]) == pace.PACE_EINVAL       # repeated sequence
+    assert call(4, [0, 1, 2, 4]) == pace.PACE_EINVAL       # index past B
+    assert call(4, [-1, 0, 1, 2]) == pace.PACE_EINVAL
+    assert call(300, list(range(300))) == pace.PACE_EUNSUPPORTED
+    with pytest.raises(ValueError):
+        pace._lib._order(pace.LayerConfig(B=4, Hv=4, Hk=4, dk=64, dv=64, group=32), [0, 1, 2])
