@@ -580,27 +580,63 @@ def cpu_baseline(args, tiles_per_token):
     toks = make_tokens(7, Bs, 64, Hv, Hk, d, d, bf16=True)
     tiles = [(b, h) for b in range(Bs) for h in range(0, Hv, 4)]
     from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):               # one host thread: the figure is per core
-        t0 = time.time()
-        steps = 0
-        while True:
-            o, st, bu, _ = pk.decode_step_layer(ocfg, st, bu, *toks.token(steps % 64), tiles=tiles)
-            steps += 1
-            if time.time() - t0 > args.cpu_seconds and steps % dP == 0:
-                break
-        el = time.time() - t0
-    tile_steps = steps * len(tiles)
-    threads = os.environ.get("OMP_NUM_THREADS", "unset")
+
+    def rate(limit, seconds):
+        """(tile-steps, seconds, decode steps) of the oracle with BLAS at `limit` threads."""
+        nonlocal st, bu
+        with threadpool_limits(limits=limit):
+            t0 = time.time()
+            steps = 0
+            while True:
+                o, st, bu, _ = pk.decode_step_layer(ocfg, st, bu, *toks.token(steps % 64), tiles=tiles)
+                steps += 1
+                if time.time() - t0 > seconds and steps % dP == 0:
+                    break
+            return steps * len(tiles), time.time() - t0, steps
+
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    # one host thread (the reported figure), then BLAS free to use every allowed core
+    tile_steps, el, steps = rate(1, args.cpu_seconds / 2)
+    ts_all, el_all, _ = rate(None, args.cpu_seconds / 2)
+    threads = os.environ.get("OMP_NUM_THREADS", "unset")
     return {"value": round(tile_steps / el / tiles_per_token, 3), "unit": "tokens/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{tile_steps} tile-steps ({len(tiles)} (seq, head) tiles x {steps} decode steps incl. "
                       f"{steps // dP} flushes) of the PACE-4 layer shape in {el:.1f}s, single-threaded "
                       f"Python/NumPy fp64 (BLAS limited to 1 thread); tokens/s = tile-steps/s / ({tiles_per_token} tiles per token); "
-                      f"host affinity {cores} cores, OMP_NUM_THREADS={threads}"}
+                      f"host affinity {cores} cores, OMP_NUM_THREADS={threads}",
+            "all_cores": {"value": round(ts_all / el_all / tiles_per_token, 3), "unit": "tokens/s",
+                          "blas_threads": cores,
+                          "note": f"the same oracle and sample for {el_all:.1f}s with BLAS free to use all "
+                                  f"{cores} allowed cores"},
+            "tiny_reference": tiny_reference_time()}
+
+
+def tiny_reference_time():
+    """The oracle end to end on the tiny reference configuration (2 sequences, 4 heads,
+    d = 64, fp32, symmetric int4 g = 32, int8 buffer, dP = 8): a 512-token prefill in two
+    chunks, then 64 decode steps (8 flushes), one host thread."""
+    from oracle import packing as pk
+    from pace_synth import make_tokens
+    from threadpoolctl import threadpool_limits
+    ocfg = pk.LayerCfg(B=2, Hv=4, Hk=4, dk=64, dv=64, group=32, asym=False, buf="int8", dP=8, bf16_io=False)
+    toks = make_tokens(0, 2, 576, 4, 4, 64, 64)
+    tiles = [(b, h) for b in range(2) for h in range(4)]
+    with threadpool_limits(limits=1):
+        t0 = time.time()
+        state = np.zeros(pk.state_layout(ocfg)[2], dtype=np.uint8)
+        for c in range(2):
+            _, state, _ = pk.prefill_layer(ocfg, state, *toks.span(256 * c, 256 * (c + 1)), tiles=tiles)
+        buffer = np.zeros(pk.buffer_layout(ocfg)[1], dtype=np.uint8)
+        for t in range(512, 576):
+            _, state, buffer, _ = pk.decode_step_layer(ocfg, state, buffer, *toks.token(t))
+        el = time.time() - t0
+    return {"seconds": round(el, 2), "workload": "tiny reference: B=2, 4 heads, d=64, fp32, sym int4 g=32, "
+            "512-token prefill (2 chunks) + 64 decode tokens (8 flushes), oracle on one host thread",
+            "tokens_per_s": round(2 * 576 / el, 1)}
 
 
 if __name__ == "__main__":
