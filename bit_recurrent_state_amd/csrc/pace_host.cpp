@@ -33,7 +33,8 @@ pace_status validate(const pace_layer_cfg* c) {
   if (c->group != 32 && c->group != 64) return PACE_EUNSUPPORTED;
   if (c->dP > kMaxPeriod) return PACE_EUNSUPPORTED;
   if (c->Hv > kMaxHeads || c->B > 65535) return PACE_EUNSUPPORTED;
-  if (c->chunk != 256) return PACE_EUNSUPPORTED;
+  // the prefill kernels round where a 64-token sub-block ends on a multiple of the period
+  if (c->chunk % 64 != 0) return PACE_EUNSUPPORTED;
   // 4-bit zero points pack two groups of one column per byte
   if (c->state_kind == PACE_STATE_ASYM && (c->dk / c->group) % 2 != 0) return PACE_EUNSUPPORTED;
   return PACE_OK;

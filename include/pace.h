@@ -48,7 +48,8 @@
  *              retained error E_h = e_h / (1 - a_h^(2 dP)) ([p1] "How it differs").
  *
  * Rounding schedule ([p1] "How it works"; [p2] "Key Terms", periodic rounding):
- *   prefill rounds the state once per chunk of `chunk` (256) tokens and once at the
+ *   prefill rounds the state once per chunk of `chunk` tokens (256 in the method; any
+ *   multiple of 64 is accepted, since the pages never vary it) and once at the
  *   end of the call; decode appends each token to a decode buffer and rounds the
  *   state once every dP tokens (default 8), when the buffer is folded in.
  *
@@ -133,8 +134,8 @@ typedef enum { PACE_BUF_INT8 = 0, PACE_BUF_K4_VBF16 = 1 } pace_buf_kind;
 typedef enum { PACE_IO_F32 = 0, PACE_IO_BF16 = 1 } pace_io_dtype;
 
 /* One gated-delta layer.  Supported by the kernels: dk, dv in {64, 128}; g in {32, 64}
- * with g | dk (and g <= dk); 1 <= dP <= 32; chunk = 256; Hv % Hk == 0; Hv <= 64;
- * 1 <= B <= 65535. */
+ * with g | dk (and g <= dk); 1 <= dP <= 32; chunk a multiple of 64 (256 in the method);
+ * Hv % Hk == 0; Hv <= 64; 1 <= B <= 65535. */
 typedef struct {
   int32_t B, Hv, Hk, dk, dv;
   int32_t group;        /* g: key-axis elements per scale group */

@@ -86,6 +86,37 @@ def test_prefill_chunks_match_oracle(name):
     check_prefill_call(ocfg, gcfg, s1, toks.span(256, 356), tiles, name + "/partial")
 
 
+@pytest.mark.parametrize("name,chunk", [("pace48_g32_bf16", 64), ("pace48_g32_bf16", 512),
+                                        ("tiny_sym4_g32_f32", 128)])
+def test_prefill_rounding_period(name, chunk):
+    """Prefill rounding periods other than 256 (multiples of 64), on the warp-specialised
+    kernel (bf16, d = 128) and the four-wave kernel (fp32, d = 64):
+      * one call of `chunk` tokens from the oracle's rounded state (one rounding, at its
+        end) matches the oracle -- the parity protocol, which starts every rounding from
+        the oracle's state;
+      * one call over 600 tokens equals `chunk`-token calls issued one after another, bit
+        for bit (outputs and packed state), so it rounds exactly after every `chunk` tokens
+        and after the last."""
+    print(f"[prefill parity] case={name} chunk={chunk}", flush=True)
+    B, Hv, Hk, d, g, asym, bf16, hb = PCASES[name]
+    ocfg = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=g, asym=asym, buf="int8", dP=8,
+                       bf16_io=bf16, head_bits=hb, chunk=chunk)
+    gcfg = _lib().LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=g, asym=asym, buf="int8",
+                              bf16_io=bf16, dP=8, head_bits=hb, chunk=chunk)
+    toks = make_tokens(500 + chunk, B, 856, Hv, Hk, d, d, bf16=bf16)
+    tiles = [(b, h) for b in range(B) for h in range(Hv)]
+    zero = np.zeros(pk.state_layout(ocfg)[2], dtype=np.uint8)
+    _, s1, _ = pk.prefill_layer(ocfg, zero, *toks.span(0, 256), tiles=tiles)
+    check_prefill_call(ocfg, gcfg, s1, toks.span(256, 256 + chunk), tiles, f"{name}/chunk{chunk}")
+    o_all, s_all = gpu_prefill(gcfg, s1, toks.span(256, 856))
+    st, outs = s1, []
+    for t0 in range(256, 856, chunk):
+        o, st = gpu_prefill(gcfg, st, toks.span(t0, min(t0 + chunk, 856)))
+        outs.append(o)
+    assert np.array_equal(s_all, st), "packed state after one call differs from per-period calls"
+    assert np.array_equal(o_all, np.concatenate(outs, axis=1)), "outputs differ"
+
+
 @pytest.mark.parametrize("T", [1, 5, 64, 65])
 def test_prefill_short_prompts(T):
     """Prompts of at most one 64-token sub-block and just past it (one sub-block, so the

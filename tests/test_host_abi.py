@@ -110,7 +110,7 @@ def test_validation_errors():
         with pytest.raises(pace.PaceError) as ei:
             pace.layout(c)
         assert ei.value.status == pace.PACE_EINVAL, kw
-    unsupported = [dict(dk=96, dv=96, group=32), dict(dP=33), dict(Hv=128, Hk=128), dict(chunk=128),
+    unsupported = [dict(dk=96, dv=96, group=32), dict(dP=33), dict(Hv=128, Hk=128), dict(chunk=100),
                    dict(dk=128, dv=64),
                    # asymmetric 4-bit zero points are packed two a byte within a column, so
                    # the number of groups per column must be even
@@ -122,6 +122,8 @@ def test_validation_errors():
         with pytest.raises(pace.PaceError) as ei:
             pace.layout(c)
         assert ei.value.status == pace.PACE_EUNSUPPORTED, kw
+    for chunk in (64, 128, 512):                 # prefill rounding periods: multiples of 64
+        pace.layout(pace.LayerConfig(B=2, Hv=4, Hk=4, dk=64, dv=64, group=32, chunk=chunk))
     c = pace.LayerConfig(B=2, Hv=4, Hk=4, dk=64, dv=64, group=32, head_bits=[4, 5, 4, 4])
     with pytest.raises(pace.PaceError):
         pace.layout(c)
