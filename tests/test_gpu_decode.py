@@ -160,7 +160,19 @@ def test_decode_full_size_sampled(name):
     sequences, bf16, dP = 8) with random per-sequence counts.  Sampled tiles (both value
     heads of a key head, flushing and appending sequences) are compared with the oracle;
     every tile's count is checked against the rule count' = count + 1, or 0 on a flush."""
-    print(f"[decode full size] case={name}", flush=True)
+    full_size_case(name, ordered=False)
+
+
+@pytest.mark.parametrize("name", ["pace4_b64", "pace48_int8_b64"])
+def test_ordered_decode_full_size_sampled(name):
+    """The same at full size through pace_decode_step_ordered, in the launch configuration
+    of the benchmark's continuous-batching leg: the sequences that flush at this step
+    placed first, the others after them."""
+    full_size_case(name, ordered=True)
+
+
+def full_size_case(name, ordered):
+    print(f"[decode full size] case={name} ordered={ordered}", flush=True)
     B, Hv, Hk, d, g, asym, buf, hb = FULL[name]
     if hb == "quarter":
         hb = [8 if h % 4 == 1 else 4 for h in range(Hv)]
@@ -179,7 +191,11 @@ def test_decode_full_size_sampled(name):
     seqs = [0, 1, 2, B // 2, B // 2 + 3, B - 1]
     tiles = [(b, h) for b in seqs for h in (0, 1, 14, 15, Hv - 2, Hv - 1)]
     o_ref, s_ref, b_ref, pre = pk.decode_step_layer(ocfg, state, buffer, *toks.token(0), tiles=tiles)
-    o_gpu, s_gpu, b_gpu = run_gpu_decode(gcfg, state, buffer, toks)
+    order = None
+    if ordered:
+        flushing = np.asarray(counts) == dP - 1
+        order = np.concatenate([np.flatnonzero(flushing), np.flatnonzero(~flushing)])
+    o_gpu, s_gpu, b_gpu = run_gpu_decode(gcfg, state, buffer, toks, order=order)
     parity.check_outputs(o_gpu, o_ref, tiles, name, out_bf16=True)
     assert len(pre) > 0
     qg = pk.unpack_state(ocfg, s_gpu, list(pre.keys()))
