@@ -59,8 +59,7 @@ def _load():
                                     ctypes.POINTER(ctypes.c_double), ctypes.c_int32,
                                     ctypes.POINTER(ctypes.c_int8), ctypes.POINTER(ctypes.c_double)]
     lib.pace_prefill_chunk.argtypes = [C, P, P, P, P, P, P, ctypes.c_int32, P, P, ctypes.c_size_t, P]
-    lib.pace_prefill_workspace_bytes.argtypes = [C, ctypes.c_int32]
-    lib.pace_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.pace_prefill_workspace_bytes.argtypes = [C, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.pace_decode_step.argtypes = [C, P, P, P, P, P, P, P, P, P, P]
     lib.pace_decode_step_ordered.argtypes = [C, P, P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_int32), P, P]
     lib.pace_flush_requant.argtypes = [C, P, P, P, P]
@@ -68,7 +67,8 @@ def _load():
     lib.pace_calibrate_heads.argtypes = [C, P, P, P, P, ctypes.c_int32, P, P, P]
     lib.pace_status_str.argtypes = [ctypes.c_int]
     lib.pace_status_str.restype = ctypes.c_char_p
-    for name in ["pace_layout", "pace_head_alloc", "pace_prefill_chunk", "pace_decode_step",
+    for name in ["pace_layout", "pace_head_alloc", "pace_prefill_chunk", "pace_prefill_workspace_bytes",
+                 "pace_decode_step",
                  "pace_decode_step_ordered", "pace_flush_requant", "pace_bf16_decode_step", "pace_calibrate_heads"]:
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -216,7 +216,9 @@ def flush_requant(cfg: LayerConfig, state, buffer, seq_mask=None, stream=None):
 
 def prefill_workspace_bytes(cfg: LayerConfig, T: int) -> int:
     c = cfg._c()
-    return int(LIB.pace_prefill_workspace_bytes(ctypes.byref(c), T))
+    out = ctypes.c_size_t(0)
+    _check(LIB.pace_prefill_workspace_bytes(ctypes.byref(c), T, ctypes.byref(out)), "pace_prefill_workspace_bytes")
+    return int(out.value)
 
 
 def prefill_chunk(cfg: LayerConfig, state, q, k, v, a, beta, o, workspace=None, stream=None):

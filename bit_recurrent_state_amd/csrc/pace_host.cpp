@@ -125,9 +125,12 @@ pace_status pace_head_alloc(int32_t Hv, int32_t dP, const double* e_h, const dou
   return PACE_OK;
 }
 
-size_t pace_prefill_workspace_bytes(const pace_layer_cfg* cfg, int32_t T) {
-  if (validate(cfg) != PACE_OK || T <= 0) return 0;
-  return prefill_workspace_bytes(cfg->B, cfg->Hv, cfg->dk, cfg->dv, T, cfg->chunk);
+pace_status pace_prefill_workspace_bytes(const pace_layer_cfg* cfg, int32_t T, size_t* bytes_out) {
+  if (!bytes_out || T <= 0) return PACE_EINVAL;
+  const pace_status st = validate(cfg);
+  if (st != PACE_OK) return st;
+  *bytes_out = prefill_workspace_bytes(cfg->B, cfg->Hv, cfg->dk, cfg->dv, T, cfg->chunk);
+  return PACE_OK;
 }
 
 namespace {
@@ -162,6 +165,8 @@ pace_status decode_step(const pace_layer_cfg* cfg, void* state, void* buffer, co
   p.io_bf16 = cfg->io_dtype == PACE_IO_BF16;
   SeqOrder order{};
   if (seq_order) {
+    // only the specialised kernels take an order (see launch_decode)
+    if (!(cfg->dk == 128 && cfg->dP <= 8 && cfg->io_dtype == PACE_IO_BF16)) return PACE_EUNSUPPORTED;
     // a permutation of 0..B-1, checked here so that the kernel can trust it
     if (cfg->B > kMaxOrderedBatch) return PACE_EUNSUPPORTED;
     uint8_t seen[kMaxOrderedBatch] = {};

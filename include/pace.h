@@ -208,8 +208,11 @@ pace_status pace_prefill_chunk(const pace_layer_cfg* cfg, void* state, const voi
                                const float* beta, int32_t T, void* o, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* Workspace bytes pace_prefill_chunk needs for T tokens (0 if it needs none). */
-size_t pace_prefill_workspace_bytes(const pace_layer_cfg* cfg, int32_t T);
+/* Workspace bytes pace_prefill_chunk needs for T tokens of this configuration, written to
+ * *bytes_out (0: the call needs no workspace and accepts workspace == NULL).  Host only.
+ * Errors (nothing is written): PACE_EINVAL for a null pointer, T < 1 or a malformed
+ * config; PACE_EUNSUPPORTED for a configuration the kernels do not implement. */
+pace_status pace_prefill_workspace_bytes(const pace_layer_cfg* cfg, int32_t T, size_t* bytes_out);
 
 /* One decode step ([p1] "How it works": decode buffer, round once per dP tokens;
  * [p2] "Key Terms": decode buffer, periodic rounding).  For every active sequence and
@@ -231,10 +234,13 @@ pace_status pace_decode_step(const pace_layer_cfg* cfg, void* state, void* buffe
  * are started first and spread one per compute unit (place those whose buffer holds dP-1
  * tokens, i.e. that flush at this step, first).  It is copied into the launch, so the
  * array may be reused at once (and a captured graph keeps the order it was captured with).
- * The order is applied by the kernels of the layouts the method names (dk = 128,
- * dP <= 8, bf16 I/O); other configurations run in launch order.
- * Errors: PACE_EINVAL for a null seq_order or one that is not a permutation of 0..B-1,
- * PACE_EUNSUPPORTED for B > 256; otherwise as pace_decode_step. */
+ * Only the kernels of the layouts the method names apply an order: dk = dv = 128, dP <= 8,
+ * bf16 I/O (any state kind, head map and buffer kind).  Other layouts are rejected rather
+ * than run in launch order, so that a caller never believes its order took effect when it
+ * did not.
+ * Errors: PACE_EINVAL for a null seq_order or one that is not a permutation of 0..B-1;
+ * PACE_EUNSUPPORTED for B > 256 or a layout outside the one above; otherwise as
+ * pace_decode_step. */
 pace_status pace_decode_step_ordered(const pace_layer_cfg* cfg, void* state, void* buffer,
                                      const void* q, const void* k, const void* v, const float* a,
                                      const float* beta, const uint8_t* active,

@@ -305,6 +305,33 @@ def _bf16_ref_step(S, q, k, v, a, beta):
     return S2, po.readout(S2, q)
 
 
+def bf16_state_bits_check(S_gpu, S_new, S_old, k, v, a, beta):
+    """Stored bf16 state against round-to-nearest-even of the oracle's fp64 update.
+
+    Every stored value must equal bf16_rne(S') bit for bit, except a one-ulp step to the
+    other neighbour where S' lies within the fp32 evaluation error of the midpoint between
+    them (the kernel forms S' in fp32 and rounds that): the window is 2^-18 of the
+    magnitudes that enter the element, a_t |S_ij| + |k_i| beta (|v_j| + a_t sum_k |S_kj k_k|),
+    i.e. 64 fp32 ulps of the largest term.  Returns the number of such flips."""
+    want = po.bf16_rne(S_new)
+    bad = np.nonzero(S_gpu != want)
+    if bad[0].size == 0:
+        return 0
+    Sabs = np.abs(S_old)
+    U = beta * (np.abs(v) + a * (Sabs.T @ np.abs(k)))                 # [dv]
+    tol = 2.0 ** -18 * (a * Sabs + np.outer(np.abs(k), U))
+    for i, j in zip(*bad):
+        g, w, x = float(S_gpu[i, j]), float(want[i, j]), float(S_new[i, j])
+        # the bf16 value next to w in the direction of g
+        up = g > w
+        nudge = max(abs(w) * 2.0 ** -20, 2.0 ** -140)
+        nxt = float(po.bf16_ceil(w + nudge)) if up else -float(po.bf16_ceil(-w + nudge))
+        assert g == nxt, f"stored {g!r} is not a bf16 neighbour of {w!r} (x = {x!r})"
+        assert abs(x - 0.5 * (g + w)) <= tol[i, j], \
+            f"stored {g!r} vs rne {w!r}: x = {x!r} is {abs(x - 0.5 * (g + w)):.3g} from the midpoint (window {tol[i, j]:.3g})"
+    return int(bad[0].size)
+
+
 # (the 8 x 32-head case holds 8 MiB of bf16 state, where the kernel streams the state with
 # non-temporal accesses; the others use ordinary accesses)
 @pytest.mark.parametrize("bf16_io,d,B,Hv,Hk", [(True, 128, 3, 8, 4), (False, 64, 3, 8, 4), (True, 128, 8, 32, 16)])
@@ -320,14 +347,17 @@ def test_bf16_baseline_matches_oracle(bf16_io, d, B, Hv, Hk):
     o = torch.empty((B, Hv, d), dtype=torch.bfloat16 if bf16_io else torch.float32, device="cuda")
     pace.bf16_decode_step(cfg, st, io_dev(q, bf16_io), io_dev(k, bf16_io), io_dev(v, bf16_io), dev(a), dev(beta), o)
     torch.cuda.synchronize()
-    S_gpu = host(st)
+    S_gpu = host(st).astype(np.float64)
     o_gpu = host(o)
+    flips = 0
     for b in range(B):
         for h in range(Hv):
             kh = h // (Hv // Hk)
-            S2, oo = _bf16_ref_step(S[b, h].T, q[b, kh], k[b, kh], v[b, h], float(a[b, h]), float(beta[b, h]))
+            S_old = S[b, h].T                                           # [key, col]
+            S2, oo = _bf16_ref_step(S_old, q[b, kh], k[b, kh], v[b, h], float(a[b, h]), float(beta[b, h]))
             assert parity.rel_err_io(o_gpu[b, h], oo, bf16_io) <= parity.TOL_REL
-            # stored state = bf16 rounding of the updated state (one bf16 ulp allowed for
-            # fp32-vs-fp64 differences at rounding boundaries)
-            err = np.abs(S_gpu[b, h].T - S2)
-            assert np.all(err <= np.abs(S2) * 2.0 ** -7 + 1e-6)
+            flips += bf16_state_bits_check(S_gpu[b, h].T, S2, S_old, np.asarray(k[b, kh], np.float64),
+                                           np.asarray(v[b, h], np.float64), float(a[b, h]), float(beta[b, h]))
+    n = B * Hv * d * d
+    print(f"[bf16 baseline parity] {flips} rounding-window flips in {n} stored values", flush=True)
+    assert flips <= 1e-4 * n + 1

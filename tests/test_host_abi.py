@@ -159,8 +159,8 @@ def test_sequence_order_validated_before_any_launch():
     L = pace._lib
     fake = ctypes.c_void_p(0x10000)
 
-    def call(B, order):
-        c = pace.LayerConfig(B=B, Hv=4, Hk=4, dk=64, dv=64, group=32)._c()
+    def call(B, order, d=128, bf16_io=True, dP=8):
+        c = pace.LayerConfig(B=B, Hv=4, Hk=4, dk=d, dv=d, group=32, bf16_io=bf16_io, dP=dP)._c()
         ptr = None if order is None else np.asarray(order, dtype=np.int32).ctypes.data_as(
             ctypes.POINTER(ctypes.c_int32))
         return L.LIB.pace_decode_step_ordered(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake,
@@ -171,5 +171,30 @@ def test_sequence_order_validated_before_any_launch():
     assert call(4, [0, 1, 2, 4]) == pace.PACE_EINVAL       # index past B
     assert call(4, [-1, 0, 1, 2]) == pace.PACE_EINVAL
     assert call(300, list(range(300))) == pace.PACE_EUNSUPPORTED
+    # layouts whose kernels do not apply an order are refused, never run in launch order
+    assert call(4, [3, 2, 1, 0], d=64) == pace.PACE_EUNSUPPORTED
+    assert call(4, [3, 2, 1, 0], bf16_io=False) == pace.PACE_EUNSUPPORTED
+    assert call(4, [3, 2, 1, 0], dP=12) == pace.PACE_EUNSUPPORTED
     with pytest.raises(ValueError):
         pace._lib._order(pace.LayerConfig(B=4, Hv=4, Hk=4, dk=64, dv=64, group=32), [0, 1, 2])
+
+
+def test_prefill_workspace_query_distinguishes_errors_from_zero():
+    """pace_prefill_workspace_bytes returns a status: an invalid or unsupported
+    configuration is an error (and writes nothing), a valid one writes its size."""
+    pace = _pace()
+    L = pace._lib
+    out = ctypes.c_size_t(12345)
+    good = pace.LayerConfig(B=2, Hv=4, Hk=4, dk=64, dv=64, group=32)._c()
+    assert L.LIB.pace_prefill_workspace_bytes(ctypes.byref(good), 256, ctypes.byref(out)) == pace.PACE_OK
+    assert out.value == 0                     # the kernels keep every intermediate on chip
+    out.value = 12345
+    bad = pace.LayerConfig(B=2, Hv=4, Hk=3, dk=64, dv=64, group=32)._c()        # Hv % Hk != 0
+    assert L.LIB.pace_prefill_workspace_bytes(ctypes.byref(bad), 256, ctypes.byref(out)) == pace.PACE_EINVAL
+    uns = pace.LayerConfig(B=2, Hv=4, Hk=4, dk=96, dv=96, group=32)._c()        # no kernel for d = 96
+    assert L.LIB.pace_prefill_workspace_bytes(ctypes.byref(uns), 256, ctypes.byref(out)) == pace.PACE_EUNSUPPORTED
+    assert L.LIB.pace_prefill_workspace_bytes(ctypes.byref(good), 0, ctypes.byref(out)) == pace.PACE_EINVAL
+    assert L.LIB.pace_prefill_workspace_bytes(ctypes.byref(good), 256, None) == pace.PACE_EINVAL
+    assert out.value == 12345
+    with pytest.raises(pace.PaceError):
+        pace.prefill_workspace_bytes(pace.LayerConfig(B=2, Hv=4, Hk=3, dk=64, dv=64, group=32), 256)
