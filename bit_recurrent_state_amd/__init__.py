@@ -11,4 +11,4 @@ from ._lib import (  # noqa: F401
     prepare_decode_step, prepare_bf16_decode_step, prepare_prefill_chunk,
     PACE_OK, PACE_EINVAL, PACE_EUNSUPPORTED, PACE_EHIP,
 )
-from .presets import pace4, pace48, tiny_ref  # noqa: F401
+from .presets import bf16_periodic, pace4, pace48, tiny_ref  # noqa: F401

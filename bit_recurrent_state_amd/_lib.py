@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpace.so")
 
 PACE_OK, PACE_EINVAL, PACE_EUNSUPPORTED, PACE_EHIP = 0, -1, -2, -3
-STATE_SYM, STATE_ASYM = 0, 1
+STATE_SYM, STATE_ASYM, STATE_BF16 = 0, 1, 2
 BUF_INT8, BUF_K4_VBF16 = 0, 1
 IO_F32, IO_BF16 = 0, 1
 
@@ -49,6 +49,11 @@ EXPORTS = ["pace_layout", "pace_head_alloc", "pace_calibrate_heads", "pace_prefi
 
 
 def _load():
+    # torch ships its own HIP runtime, under the same soname as ROCm's.  Load torch first
+    # so that libpace.so binds to that runtime: loaded the other way round, the process
+    # can hold two HIP runtimes, and kernels launched through one on memory allocated
+    # through the other fail.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m bit_recurrent_state_amd.build` (hipcc, gfx950)")
@@ -101,13 +106,14 @@ class LayerConfig:
     dP: int = 8
     chunk: int = 256
     head_bits: Optional[Sequence[int]] = None
+    bf16_state: bool = False     # state kept as bf16 values (PACE_STATE_BF16)
 
     def _c(self):
         hb = None
         if self.head_bits is not None:
             hb = (ctypes.c_int8 * self.Hv)(*[int(x) for x in self.head_bits])
         cfg = _Cfg(self.B, self.Hv, self.Hk, self.dk, self.dv, self.group,
-                   STATE_ASYM if self.asym else STATE_SYM,
+                   STATE_BF16 if self.bf16_state else (STATE_ASYM if self.asym else STATE_SYM),
                    BUF_INT8 if self.buf == "int8" else BUF_K4_VBF16,
                    IO_BF16 if self.bf16_io else IO_F32, self.dP, self.chunk,
                    ctypes.cast(hb, ctypes.POINTER(ctypes.c_int8)) if hb is not None else None)

@@ -43,6 +43,7 @@ namespace {
 constexpr int kWaves = 2;
 constexpr int kThreads = 64 * kWaves;
 
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -136,6 +137,25 @@ __device__ inline int sum8(long v) {
   return __builtin_amdgcn_sdot4(hi, 0x01010101, __builtin_amdgcn_sdot4(lo, 0x01010101, 0, false), false);
 }
 
+// x as three int8 pieces with power-of-two scales s1, s1/128, s1/16384, where
+// s1 = 2^(e-6) for the vector's max |x| = M = m 2^e (0.5 <= m < 1), so |x / s1| < 64 and every
+// piece fits in int8.  The pieces reproduce x to within s1 / 32768 = 2^(e-21), i.e. exactly
+// down to 2^-20 of M (elements more than 2^12 times smaller than M lose their low bits).
+// Returns the exponent of s1 in *e1 (0 for M = 0, when every piece is 0).
+__device__ inline void int8_pieces(float x, float M, float& p1, float& p2, float& p3, int& e1) {
+  p1 = p2 = p3 = 0.f;
+  e1 = 0;
+  if (M > 0.f) {
+    frexpf(M, &e1);
+    e1 -= 6;
+    p1 = rintf(ldexpf(x, -e1));
+    const float r1 = x - ldexpf(p1, e1);
+    p2 = rintf(ldexpf(r1, 7 - e1));
+    const float r2 = r1 - ldexpf(p2, e1 - 7);
+    p3 = rintf(ldexpf(r2, 14 - e1));
+  }
+}
+
 // Shared memory of one workgroup.  TOK = largest decode period this instantiation
 // serves; vector slots 0..TOK-1 are buffered tokens, TOK..TOK+2 the pieces of q.
 // Row strides are padded (codes: +16 bytes, projections: +4 floats) so that the 16 lanes
@@ -171,6 +191,9 @@ struct alignas(16) Smem {
 // GT: scale-group size (32 or 64), 0 = taken from the parameters at run time.
 // AS: 0 = symmetric, 1 = asymmetric, 2 = taken from the parameters at run time.
 // NTS: the state's codes, scales and zero points are read and written non-temporally.
+// BFS: the state is bf16 values (one dv x dk record per head, value-column-major): the
+//      same buffer, replay and flush schedule, with bf16 matrix-core projections and a
+//      flush that rounds each element to the nearest bf16.
 // Second kernel argument: the sequence order of ordered launches, nothing otherwise (so
 // that launches in plain order keep their argument block and their first addresses need
 // no extra load).
@@ -179,10 +202,10 @@ struct OrderArg : SeqOrder {};
 template <>
 struct OrderArg<false> {};
 
-template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS, bool ORD = false>
+template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS, bool ORD = false, bool BFS = false>
 // Eight resident workgroups per CU (four waves per SIMD) for the specialised dP <= 8
-// variants, so a 2048-tile launch runs in one round: at most 128 VGPRs.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOK <= 8 && GT != 0 ? 4 : 1)))
+// packed-state variants, so a 2048-tile launch runs in one round: at most 128 VGPRs.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!BFS && TOK <= 8 && GT != 0 ? 4 : 1)))
 void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
   using SM = Smem<D, TOK>;
   constexpr int NV = SM::NV;
@@ -221,7 +244,7 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
   const int count_raw = *countp;
   __builtin_amdgcn_sched_barrier(0);          // issue the count load first
 
-  const bool is8 = HB == 8 ? true : (HB == 4 ? false : ((p.mask8 >> h) & 1ull) != 0);
+  const bool is8 = BFS ? false : (HB == 8 ? true : (HB == 4 ? false : ((p.mask8 >> h) & 1ull) != 0));
   const int bits = is8 ? 8 : 4;
   const uint64_t below = h ? (p.mask8 & ((1ull << h) - 1ull)) : 0ull;
   const uint64_t n8 = (uint64_t)__popcll(below);
@@ -231,7 +254,7 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
   const int group = GT ? GT : p.group;
   const int NG = D / group;
   const int kpg = group / 32;           // MFMA blocks per scale group
-  const int cbytes = D * bits / 8;      // bytes per state column
+  const int cbytes = BFS ? 2 * D : D * bits / 8;   // bytes per state column
   const bool asym = AS == 2 ? (p.asym != 0) : (AS == 1);
   const bool flush_only = p.flush_only != 0;
 
@@ -284,8 +307,11 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
   // instead of a zero-point region they do not have)
   const int sc_vec = D * NG * 2 / 16;
   const int zp_vec = asym ? D * NG * bits / 8 / 16 : 1;
-  const uint4 sc_reg = ld_state<NTS>((const uint4*)g_scales + min(tid, sc_vec - 1));
-  const uint4 zp_reg = ld_state<NTS>((const uint4*)(asym ? (const uint8_t*)g_zeros : (const uint8_t*)g_scales) + min(tid, zp_vec - 1));
+  uint4 sc_reg = make_uint4(0, 0, 0, 0), zp_reg = make_uint4(0, 0, 0, 0);
+  if constexpr (!BFS) {
+    sc_reg = ld_state<NTS>((const uint4*)g_scales + min(tid, sc_vec - 1));
+    zp_reg = ld_state<NTS>((const uint4*)(asym ? (const uint8_t*)g_zeros : (const uint8_t*)g_scales) + min(tid, zp_vec - 1));
+  }
 
   // counts outside [0, dP) cannot come from this library; clamp so that every slot
   // index stays inside the buffer whatever the buffer holds
@@ -306,6 +332,39 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
       if (i >= early * VV && i < vvec) vvl[it] = v_buf[i];
     }
   }
+  // State codes of this lane, strip by strip: strip st = wave + kWaves * s, column
+  // st*16 + l16, keys of quarter qq (units qq*KB .. qq*KB + KB - 1).
+  // (bf16 state: keys 32 kb + 8 qq .. + 7 of the column, 16 bytes per 32-key block)
+  constexpr int AW = BFS ? 4 * KB : (HB == 4 ? KB : 2 * KB);   // state dwords per strip and lane
+  uint32_t araw[SPW][AW];
+  auto load_state = [&]() {
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const int c = (wave + kWaves * s) * 16 + l16;
+      const uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
+      if constexpr (BFS) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const uint4 v = ld_state<NTS>(rec + (size_t)c * cbytes + (32 * kb + 8 * qq) * 2);
+          araw[s][4 * kb] = v.x; araw[s][4 * kb + 1] = v.y; araw[s][4 * kb + 2] = v.z; araw[s][4 * kb + 3] = v.w;
+        }
+      } else if (!is8) {
+        if constexpr (KB == 4) {
+          const uint4 v = ld_state<NTS>(colp);
+          araw[s][0] = v.x; araw[s][1] = v.y; araw[s][2] = v.z; araw[s][3] = v.w;
+        } else {
+          const uint2 v = ld_state2<NTS>(colp);
+          araw[s][0] = v.x; araw[s][1] = v.y;
+        }
+      } else if constexpr (HB != 4) {
+#pragma unroll
+        for (int kb = 0; kb < KB; kb += 2) {
+          const uint4 v = ld_state<NTS>(colp + kb * 8);
+          araw[s][2 * kb] = v.x; araw[s][2 * kb + 1] = v.y; araw[s][2 * kb + 2] = v.z; araw[s][2 * kb + 3] = v.w;
+        }
+      }
+    }
+  };
   // keep the scheduler from pulling the first uses of the token (and their waits)
   // above the remaining load issues
   __builtin_amdgcn_sched_barrier(0);
@@ -345,19 +404,10 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
       } else {
         sm.v.b[n0][tid] = (uint16_t)pk_bf16(vx, 0.f);
       }
-      // q as three exact int8 pieces with power-of-two scales s1, s1/128, s1/16384,
-      // s1 = 2^(e-6) for max|q| = m 2^e (0.5 <= m < 1), so |q / s1| < 64
-      float q1 = 0.f, q2 = 0.f, q3 = 0.f;
-      int e1 = 0;
-      if (Mq > 0.f) {
-        frexpf(Mq, &e1);
-        e1 -= 6;
-        q1 = rintf(ldexpf(qx, -e1));
-        const float r1 = qx - ldexpf(q1, e1);
-        q2 = rintf(ldexpf(r1, 7 - e1));
-        const float r2 = r1 - ldexpf(q2, e1 - 7);
-        q3 = rintf(ldexpf(r2, 14 - e1));
-      }
+      // q as three int8 pieces with power-of-two scales (q itself is not rounded)
+      float q1, q2, q3;
+      int e1;
+      int8_pieces(qx, Mq, q1, q2, q3, e1);
       sm.kc[QS + 0][tid] = (int8_t)q1;
       sm.kc[QS + 1][tid] = (int8_t)q2;
       sm.kc[QS + 2][tid] = (int8_t)q3;
@@ -448,7 +498,7 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
   // vector read), zero points [col][group] (the four groups of the lane's A-operand
   // column are one read)
   const int lng = NG == 4 ? 2 : NG - 1;      // log2 NG (NG in {1, 2, 4})
-  if (tid < sc_vec) {                       // 8 bf16 scales [col][group] -> fp32
+  if (!BFS && tid < sc_vec) {               // 8 bf16 scales [col][group] -> fp32
     const uint32_t w[4] = {sc_reg.x, sc_reg.y, sc_reg.z, sc_reg.w};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -457,7 +507,7 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
       sm.scf[e & (NG - 1)][e >> lng] = bits_f32(u);
     }
   }
-  if (asym && tid < zp_vec) {
+  if (!BFS && asym && tid < zp_vec) {
     const uint32_t w[4] = {zp_reg.x, zp_reg.y, zp_reg.z, zp_reg.w};
     if (is8) {                               // 16 zero points, a byte each
 #pragma unroll
@@ -473,34 +523,10 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
       }
     }
   }
-  // State codes of this lane, strip by strip: strip st = wave + kWaves * s, column
-  // st*16 + l16, keys of quarter qq (units qq*KB .. qq*KB + KB - 1).  Requested only now,
-  // with the token phase done: the token-sized loads of every tile (current token,
-  // buffer, scales) are then served ahead of the state stream, and each tile meets its
-  // codes with nothing left to do but the projections.
-  constexpr int AW = HB == 4 ? KB : 2 * KB;   // code dwords per strip and lane
-  uint32_t araw[SPW][AW];
-#pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    const int c = (wave + kWaves * s) * 16 + l16;
-    const uint8_t* colp = rec + (size_t)c * cbytes + qq * KB * bits;
-    if (!is8) {
-      if constexpr (KB == 4) {
-        const uint4 v = ld_state<NTS>(colp);
-        araw[s][0] = v.x; araw[s][1] = v.y; araw[s][2] = v.z; araw[s][3] = v.w;
-      } else {
-        const uint2 v = ld_state2<NTS>(colp);
-        araw[s][0] = v.x; araw[s][1] = v.y;
-      }
-    } else if constexpr (HB != 4) {
-#pragma unroll
-      for (int kb = 0; kb < KB; kb += 2) {
-        const uint4 v = ld_state<NTS>(colp + kb * 8);
-        araw[s][2 * kb] = v.x; araw[s][2 * kb + 1] = v.y; araw[s][2 * kb + 2] = v.z; araw[s][2 * kb + 3] = v.w;
-      }
-    }
-  }
-
+  // The state codes are requested only now, with the token phase done: the token-sized
+  // loads of every tile (current token, buffer, scales) are then served ahead of the
+  // state stream.
+  load_state();
   if (n0 > early) fill_slots(early, n0, std::true_type{});   // (loads issued before the state's)
 
   __syncthreads();
@@ -522,19 +548,9 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
   v4i zacc[NT][4];
   const long zrow = asym ? (is8 ? 0x0101010101010101l : 0l) : (is8 ? 0l : (long)0xF8F8F8F8F8F8F8F8ull);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) bop[nt][kb] = *(const long*)&sm.kc[nt * 16 + l16][32 * kb + 8 * qq];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) zacc[nt][g] = v4i{0, 0, 0, 0};
-    if (zrow != 0) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          if (kb / kpg == g) zacc[nt][g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(zrow, bop[nt][kb], zacc[nt][g], 0, 0, 0);
-    }
-  }
   if (wave == kWaves - 1) {
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
@@ -562,7 +578,55 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
 
   // ------------------------------------------------------------ projections
 #pragma unroll
-  for (int s = 0; s < SPW; ++s) {
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) zacc[nt][g] = v4i{0, 0, 0, 0};
+    if (!BFS && zrow != 0) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          if (kb / kpg == g) zacc[nt][g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(zrow, bop[nt][kb], zacc[nt][g], 0, 0, 0);
+    }
+  }
+  if constexpr (BFS) {
+    // bf16 state: the stored columns are the A operand as they are, the slot codes (int8,
+    // exact in bf16) the B operand, fp32 accumulation; no scale groups
+    v8bf bb[NT][KB];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const unsigned long x = (unsigned long)bop[nt][kb];
+        uint32_t w4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w4[e] = pk_bf16((float)(int8_t)(x >> (16 * e)), (float)(int8_t)(x >> (16 * e + 8)));
+        __builtin_memcpy(&bb[nt][kb], w4, 16);
+      }
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const int ocol = (wave + kWaves * s) * 16 + 4 * qq;
+      v4f accf[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) accf[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        v8bf sa;
+        __builtin_memcpy(&sa, &araw[s][4 * kb], 16);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) accf[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa, bb[nt][kb], accf[nt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int vi = nt * 16 + l16;
+        const float vsc = sm.vscale[vi];
+        *(float4*)&sm.pw.P[vi][ocol] = make_float4(accf[nt][0] * vsc, accf[nt][1] * vsc, accf[nt][2] * vsc, accf[nt][3] * vsc);
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < (BFS ? 0 : SPW); ++s) {
     const int col0 = (wave + kWaves * s) * 16;
     const int ocol = col0 + 4 * qq;     // output columns ocol + i of this lane
     float proj[NT][4];
@@ -721,7 +785,19 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
     // accumulator tile t = 2 kb + half holds keys 32 kb + 8 qq + 4 half + i
     v4f acc[2 * KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KB && BFS; ++kb) {
+      // bf16 state: dword e of block kb holds keys 8 qq + 2e, 2e + 1 of the column
+      const uint32_t* w4 = &araw[s][4 * kb];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        acc[2 * kb][2 * i] = gn * bits_f32(w4[i] << 16);
+        acc[2 * kb][2 * i + 1] = gn * bits_f32(w4[i] & 0xFFFF0000u);
+        acc[2 * kb + 1][2 * i] = gn * bits_f32(w4[2 + i] << 16);
+        acc[2 * kb + 1][2 * i + 1] = gn * bits_f32(w4[2 + i] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < (BFS ? 0 : KB); ++kb) {
       const int g = kb / kpg;
       const float sc = sm.scf[g][c];
       const int z = asym ? (int)sm.zeros[c][g] : 1 << (bits - 1);
@@ -758,6 +834,16 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
       for (int t = 0; t < 2 * KB; ++t) ak[t] = *(const v8bf*)&sm.kT[ch][t * 16 + l16][0];
 #pragma unroll
       for (int t = 0; t < 2 * KB; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[t], bw, acc[t], 0, 0, 0);
+    }
+    if constexpr (BFS) {
+      // round every element to the nearest bf16 and write the column block back
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        st_state4<NTS>(rec + (size_t)c * cbytes + (32 * kb + 8 * qq) * 2,
+                       make_uint4(pk_bf16(acc[2 * kb][0], acc[2 * kb][1]), pk_bf16(acc[2 * kb][2], acc[2 * kb][3]),
+                                  pk_bf16(acc[2 * kb + 1][0], acc[2 * kb + 1][1]),
+                                  pk_bf16(acc[2 * kb + 1][2], acc[2 * kb + 1][3])));
+      continue;
     }
     // Requantise each (column, group) and write back in place.  Every group's range is
     // reduced over the four lanes (quarters) of the column; then each lane derives the
@@ -879,11 +965,11 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
   if (tid == 0) *countp = 0;
 }
 
-template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS = false, bool ORD = false>
+template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS = false, bool ORD = false, bool BFS = false>
 hipError_t launch_t(const DecodeParams& p, const SeqOrder* order, hipStream_t stream) {
   OrderArg<ORD> ord{};
   if constexpr (ORD) static_cast<SeqOrder&>(ord) = *order;
-  hipLaunchKernelGGL((decode_kernel<D, TOK, BUF, HB, IO, GT, AS, NTS, ORD>), dim3((unsigned)p.Hv, (unsigned)p.B),
+  hipLaunchKernelGGL((decode_kernel<D, TOK, BUF, HB, IO, GT, AS, NTS, ORD, BFS>), dim3((unsigned)p.Hv, (unsigned)p.B),
                      dim3(kThreads), 0, stream, p, ord);
   return hipGetLastError();
 }
@@ -923,6 +1009,16 @@ hipError_t launch_generic(const DecodeParams& p, hipStream_t stream) {
   return launch_t<D, 32, BUF, 0, IO, 0, 2>(p, nullptr, stream);
 }
 
+// bf16 states (int8 decode buffer): streamed by the same size rule as the packed states
+template <int D, int IO>
+hipError_t launch_bf16_state(const DecodeParams& p, hipStream_t stream) {
+  constexpr int B8 = PACE_BUF_INT8;
+  if (p.dP > 8) return launch_t<D, 32, B8, 4, IO, D, 0, false, false, true>(p, nullptr, stream);
+  if ((uint64_t)p.B * p.seq_stride >= kStreamStateBytes)
+    return launch_t<D, 8, B8, 4, IO, D, 0, true, false, true>(p, nullptr, stream);
+  return launch_t<D, 8, B8, 4, IO, D, 0, false, false, true>(p, nullptr, stream);
+}
+
 template <int BUF>
 hipError_t launch_buf(const DecodeParams& p, const SeqOrder* o, int dk, hipStream_t stream) {
   if (dk == 128 && p.dP <= 8 && p.io_bf16)
@@ -936,6 +1032,10 @@ hipError_t launch_buf(const DecodeParams& p, const SeqOrder* o, int dk, hipStrea
 hipError_t launch_decode(const DecodeParams& p, const SeqOrder* order, int dk, int dv, int buf_kind,
                          hipStream_t stream) {
   (void)dv;  // dk == dv is validated by the caller
+  if (p.bf16_state) {   // int8 buffer only (checked by the caller); never ordered
+    if (dk == 128) return p.io_bf16 ? launch_bf16_state<128, 1>(p, stream) : launch_bf16_state<128, 0>(p, stream);
+    return p.io_bf16 ? launch_bf16_state<64, 1>(p, stream) : launch_bf16_state<64, 0>(p, stream);
+  }
   if (buf_kind == PACE_BUF_INT8) return launch_buf<PACE_BUF_INT8>(p, order, dk, stream);
   return launch_buf<PACE_BUF_K4_VBF16>(p, order, dk, stream);
 }

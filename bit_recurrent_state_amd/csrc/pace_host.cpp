@@ -17,12 +17,14 @@ namespace {
 // Structural validity (PACE_EINVAL) and kernel coverage (PACE_EUNSUPPORTED).
 pace_status validate(const pace_layer_cfg* c) {
   if (!c) return PACE_EINVAL;
-  if (c->B <= 0 || c->Hv <= 0 || c->Hk <= 0 || c->dk <= 0 || c->dv <= 0 || c->group <= 0 ||
-      c->dP <= 0 || c->chunk <= 0)
+  const bool bf16_state = c->state_kind == PACE_STATE_BF16;
+  if (c->B <= 0 || c->Hv <= 0 || c->Hk <= 0 || c->dk <= 0 || c->dv <= 0 || c->dP <= 0 || c->chunk <= 0)
     return PACE_EINVAL;
   if (c->Hv % c->Hk != 0) return PACE_EINVAL;
-  if (c->dk % c->group != 0) return PACE_EINVAL;
-  if (c->state_kind != PACE_STATE_SYM && c->state_kind != PACE_STATE_ASYM) return PACE_EINVAL;
+  if (c->state_kind != PACE_STATE_SYM && c->state_kind != PACE_STATE_ASYM && !bf16_state) return PACE_EINVAL;
+  // a bf16 state has no scale groups and no per-head bit widths
+  if (bf16_state && c->head_bits) return PACE_EINVAL;
+  if (!bf16_state && (c->group <= 0 || c->dk % c->group != 0)) return PACE_EINVAL;
   if (c->buf_kind != PACE_BUF_INT8 && c->buf_kind != PACE_BUF_K4_VBF16) return PACE_EINVAL;
   if (c->io_dtype != PACE_IO_F32 && c->io_dtype != PACE_IO_BF16) return PACE_EINVAL;
   if (c->head_bits)
@@ -30,13 +32,15 @@ pace_status validate(const pace_layer_cfg* c) {
       if (c->head_bits[h] != 4 && c->head_bits[h] != 8) return PACE_EINVAL;
   // kernel coverage
   if (!((c->dk == 64 || c->dk == 128) && c->dv == c->dk)) return PACE_EUNSUPPORTED;
-  if (c->group != 32 && c->group != 64) return PACE_EUNSUPPORTED;
+  if (!bf16_state && c->group != 32 && c->group != 64) return PACE_EUNSUPPORTED;
   if (c->dP > kMaxPeriod) return PACE_EUNSUPPORTED;
   if (c->Hv > kMaxHeads || c->B > 65535) return PACE_EUNSUPPORTED;
   // the prefill kernels round where a 64-token sub-block ends on a multiple of the period
   if (c->chunk % 64 != 0) return PACE_EUNSUPPORTED;
   // 4-bit zero points pack two groups of one column per byte
   if (c->state_kind == PACE_STATE_ASYM && (c->dk / c->group) % 2 != 0) return PACE_EUNSUPPORTED;
+  // a bf16 state is served with the int8 decode buffer only
+  if (bf16_state && c->buf_kind != PACE_BUF_INT8) return PACE_EUNSUPPORTED;
   return PACE_OK;
 }
 
@@ -50,6 +54,13 @@ struct StateGeom {
 
 StateGeom state_geom(const pace_layer_cfg* c) {
   StateGeom g;
+  if (c->state_kind == PACE_STATE_BF16) {     // one dv x dk bf16 record per head
+    const uint32_t rec = (uint32_t)((size_t)c->dk * c->dv * 2);
+    g.r4 = RecordLayout{rec, 0u, 0u, rec};
+    g.r8 = g.r4;
+    g.seq_stride = (size_t)rec * c->Hv;
+    return g;
+  }
   const bool asym = c->state_kind == PACE_STATE_ASYM;
   g.r4 = record_layout(c->dk, c->dv, c->group, asym, 4);
   g.r8 = record_layout(c->dk, c->dv, c->group, asym, 8);
@@ -91,7 +102,7 @@ pace_status pace_layout(const pace_layer_cfg* cfg, pace_layout_info* out) {
   double payload = 0.0;
   for (int h = 0; h < cfg->Hv; ++h) {
     const double b = head_bits_of(cfg, h);
-    payload += b + (16.0 + (asym ? b : 0.0)) / cfg->group;
+    payload += cfg->state_kind == PACE_STATE_BF16 ? 16.0 : b + (16.0 + (asym ? b : 0.0)) / cfg->group;
   }
   out->payload_bits = payload / cfg->Hv;
   const double gamma = (double)cfg->Hv / cfg->Hk;
@@ -129,6 +140,7 @@ pace_status pace_prefill_workspace_bytes(const pace_layer_cfg* cfg, int32_t T, s
   if (!bytes_out || T <= 0) return PACE_EINVAL;
   const pace_status st = validate(cfg);
   if (st != PACE_OK) return st;
+  if (cfg->state_kind == PACE_STATE_BF16) return PACE_EUNSUPPORTED;
   *bytes_out = prefill_workspace_bytes(cfg->B, cfg->Hv, cfg->dk, cfg->dv, T, cfg->chunk);
   return PACE_OK;
 }
@@ -161,12 +173,14 @@ pace_status decode_step(const pace_layer_cfg* cfg, void* state, void* buffer, co
   p.off_a = bl.a; p.off_beta = bl.beta;
   p.B = cfg->B; p.Hv = cfg->Hv; p.Hk = cfg->Hk; p.gamma = cfg->Hv / cfg->Hk;
   p.dP = cfg->dP; p.group = cfg->group; p.asym = cfg->state_kind == PACE_STATE_ASYM;
+  p.bf16_state = cfg->state_kind == PACE_STATE_BF16;
   p.flush_only = 0;
   p.io_bf16 = cfg->io_dtype == PACE_IO_BF16;
   SeqOrder order{};
   if (seq_order) {
     // only the specialised kernels take an order (see launch_decode)
-    if (!(cfg->dk == 128 && cfg->dP <= 8 && cfg->io_dtype == PACE_IO_BF16)) return PACE_EUNSUPPORTED;
+    if (!(cfg->dk == 128 && cfg->dP <= 8 && cfg->io_dtype == PACE_IO_BF16) || cfg->state_kind == PACE_STATE_BF16)
+      return PACE_EUNSUPPORTED;
     // a permutation of 0..B-1, checked here so that the kernel can trust it
     if (cfg->B > kMaxOrderedBatch) return PACE_EUNSUPPORTED;
     uint8_t seen[kMaxOrderedBatch] = {};
@@ -220,6 +234,7 @@ pace_status pace_flush_requant(const pace_layer_cfg* cfg, void* state, void* buf
   p.off_a = bl.a; p.off_beta = bl.beta;
   p.B = cfg->B; p.Hv = cfg->Hv; p.Hk = cfg->Hk; p.gamma = cfg->Hv / cfg->Hk;
   p.dP = cfg->dP; p.group = cfg->group; p.asym = cfg->state_kind == PACE_STATE_ASYM;
+  p.bf16_state = cfg->state_kind == PACE_STATE_BF16;
   p.flush_only = 1;
   p.io_bf16 = cfg->io_dtype == PACE_IO_BF16;
   // no token: the kernel's unconditional token loads read the state instead (every index
@@ -238,6 +253,7 @@ pace_status pace_prefill_chunk(const pace_layer_cfg* cfg, void* state, const voi
   const pace_status st = validate(cfg);
   if (st != PACE_OK) return st;
   if (T <= 0 || !state || !q || !k || !v || !a || !beta || !o) return PACE_EINVAL;
+  if (cfg->state_kind == PACE_STATE_BF16) return PACE_EUNSUPPORTED;
   if (!aligned(state, 256) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
       !aligned(o, 16) || !aligned(a, 4) || !aligned(beta, 4))
     return PACE_EINVAL;
@@ -267,6 +283,7 @@ pace_status pace_calibrate_heads(const pace_layer_cfg* cfg, const void* k, const
   const pace_status st = validate(cfg);
   if (st != PACE_OK) return st;
   if (T <= 0 || !k || !v || !a || !beta || !e_h || !a_h) return PACE_EINVAL;
+  if (cfg->state_kind == PACE_STATE_BF16) return PACE_EUNSUPPORTED;
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(a, 4) || !aligned(beta, 4) ||
       !aligned(e_h, 8) || !aligned(a_h, 8))
     return PACE_EINVAL;

@@ -79,6 +79,7 @@ struct DecodeParams {
   int32_t B, Hv, Hk, gamma, dP, group, asym;
   int32_t flush_only;   // 1: pace_flush_requant (no new token)
   int32_t io_bf16;      // q, k, v, o are bf16 (else fp32)
+  int32_t bf16_state;   // the state is bf16 values (one dv x dk record per head)
 };
 
 // Sequence order of an ordered decode launch, passed by value as a second kernel argument

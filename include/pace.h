@@ -80,6 +80,18 @@
  *              nibble for even e.
  *   A zero-filled state is the all-zero state S = 0 (every scale 0).
  *
+ *   state_kind PACE_STATE_BF16 ([p1] "Assumptions and limits": in the pages' timing, most
+ *   of the decode-time gain over per-token bf16 decode comes from the decode buffer on a
+ *   bf16 state, and the 4-bit state adds the rest): the record of (b, h) is dv x dk bf16
+ *   values, value-column-major -- element (key r, column j) at bf16 index j * dk + r, the
+ *   layout of pace_bf16_decode_step -- at byte offset (b * Hv + h) * dk * dv * 2.  The
+ *   decode buffer, the replay and the once-per-dP fold are those of the packed states; a
+ *   flush rounds every element of the fp32 pre-rounding state to the nearest bf16 (ties
+ *   to even).  cfg.group is ignored, cfg.head_bits must be NULL and the buffer must be
+ *   PACE_BUF_INT8 (others: PACE_EUNSUPPORTED).  Only the decode
+ *   calls (pace_decode_step, pace_flush_requant) take this kind; pace_prefill_chunk and
+ *   pace_calibrate_heads return PACE_EUNSUPPORTED for it.  A zero-filled state is S = 0.
+ *
  * DECODE BUFFER LAYOUT (pace_layout_info.buffer_bytes per layer), regions in this
  * order, each padded to 256 bytes:
  *     count : int32 [B][Hv]   tokens buffered since the last rounding (0 .. dP-1 between
@@ -129,7 +141,11 @@ typedef enum {
   PACE_EHIP = -3           /* a HIP launch reported an error */
 } pace_status;
 
-typedef enum { PACE_STATE_SYM = 0, PACE_STATE_ASYM = 1 } pace_state_kind;
+typedef enum {
+  PACE_STATE_SYM = 0,   /* symmetric packed codes (PACE-4) */
+  PACE_STATE_ASYM = 1,  /* asymmetric packed codes with zero points (PACE-4/8) */
+  PACE_STATE_BF16 = 2   /* bf16 values: the decode buffer without the 4-bit state */
+} pace_state_kind;
 typedef enum { PACE_BUF_INT8 = 0, PACE_BUF_K4_VBF16 = 1 } pace_buf_kind;
 typedef enum { PACE_IO_F32 = 0, PACE_IO_BF16 = 1 } pace_io_dtype;
 
@@ -154,7 +170,8 @@ typedef struct {
   size_t workspace_bytes;  /* scratch needed by pace_prefill_chunk */
   size_t seq_stride;       /* bytes of state per sequence */
   double payload_bits;     /* mean over heads of b_h + (16 + z_h) / g, z_h = b_h if asym
-                              else 0 -- bits per state value ([p1] "How it differs") */
+                              else 0 -- bits per state value ([p1] "How it differs");
+                              16 for a bf16 state */
   double buffer_bits_model;  /* c * dP, c = (b_k dk / gamma + b_v dv + 32) / (dk dv)
                                 ([p1] "How it works") */
   double buffer_bits_actual; /* bytes of this buffer layout * 8 / (B Hv dk dv) */
@@ -235,7 +252,7 @@ pace_status pace_decode_step(const pace_layer_cfg* cfg, void* state, void* buffe
  * tokens, i.e. that flush at this step, first).  It is copied into the launch, so the
  * array may be reused at once (and a captured graph keeps the order it was captured with).
  * Only the kernels of the layouts the method names apply an order: dk = dv = 128, dP <= 8,
- * bf16 I/O (any state kind, head map and buffer kind).  Other layouts are rejected rather
+ * bf16 I/O, a packed state (either packed kind, any head map and buffer kind).  Other layouts are rejected rather
  * than run in launch order, so that a caller never believes its order took effect when it
  * did not.
  * Errors: PACE_EINVAL for a null seq_order or one that is not a permutation of 0..B-1;

@@ -305,6 +305,21 @@ def flush_tile(tile: TileState, requant):
 
 
 # ----------------------------------------------------------------------------------
+# Periodic decode on a bf16 state ([p1] "Assumptions and limits": in the throughput
+# study most of the decode-time reduction comes from the decode buffer with the state
+# still in bf16, and the 4-bit state reduces it further).  The buffer, the replay and the
+# once-per-dP fold are those of decode_tile_step; only the state's storage differs: it is
+# kept as bf16 values, so a flush rounds every element to the nearest bf16 (ties to
+# even), decided on the fp32 value of the pre-rounding state.  Use round_state_bf16 as
+# the `requant` of decode_tile_step / flush_tile; the tile's state is then a float array.
+# ----------------------------------------------------------------------------------
+
+def round_state_bf16(S):
+    """The bf16 state after a flush: bf16_rne of the fp32 pre-rounding state."""
+    return bf16_rne(to_f32(S))
+
+
+# ----------------------------------------------------------------------------------
 # Prefill ([p1] "How it works": the prefill rounding period is fixed to the chunk
 # kernel's chunk length, 256 tokens; [p3] "Two observations": chunked prefill kernels
 # write the state once per chunk).  Exact recurrence inside a chunk, rounding after

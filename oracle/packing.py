@@ -37,6 +37,7 @@ class LayerCfg:
     chunk: int = 256
     bf16_io: bool = False
     head_bits: Optional[Sequence[int]] = None
+    bf16_state: bool = False   # state kept as bf16 values (periodic decode on a bf16 state)
 
     @property
     def gamma(self) -> int:
@@ -49,6 +50,8 @@ class LayerCfg:
 # ------------------------------------------------------------------------- state ----
 
 def record_parts(cfg: LayerCfg, bits: int):
+    if cfg.bf16_state:                   # dv columns of dk bf16 values, nothing else
+        return cfg.dv * cfg.dk * 2, 0, 0, cfg.dv * cfg.dk * 2
     codes = cfg.dv * cfg.dk * bits // 8
     scales = cfg.dv * (cfg.dk // cfg.group) * 2
     zeros = cfg.dv * (cfg.dk // cfg.group) * bits // 8 if cfg.asym else 0
@@ -113,7 +116,11 @@ def _bytes_to_bf16(raw: np.ndarray) -> np.ndarray:
     return bits.view(np.float32).astype(np.float64)
 
 
-def pack_record(cfg: LayerCfg, qs: po.QState) -> np.ndarray:
+def pack_record(cfg: LayerCfg, qs) -> np.ndarray:
+    if cfg.bf16_state:
+        # value-column-major: element (key r, column j) at bf16 index j * dk + r
+        S = np.asarray(qs, dtype=np.float64)
+        return _bf16_to_bytes(np.ascontiguousarray(S.T).reshape(-1))
     bits = qs.bits
     c, s, z, rec = record_parts(cfg, bits)
     out = np.zeros(rec, dtype=np.uint8)
@@ -139,7 +146,10 @@ def pack_record(cfg: LayerCfg, qs: po.QState) -> np.ndarray:
     return out
 
 
-def unpack_record(cfg: LayerCfg, raw: np.ndarray, bits: int) -> po.QState:
+def unpack_record(cfg: LayerCfg, raw: np.ndarray, bits: int):
+    if cfg.bf16_state:
+        vals = _bytes_to_bf16(raw[:cfg.dv * cfg.dk * 2])
+        return vals.reshape(cfg.dv, cfg.dk).T.copy()
     c, s, z, rec = record_parts(cfg, bits)
     colb = cfg.dk * bits // 8
     codes = np.zeros((cfg.dk, cfg.dv), dtype=np.int64)
@@ -317,6 +327,8 @@ def _store_token(cfg: LayerCfg, d: dict, b: int, h: int, slot: int, k, v, a, bet
 
 
 def _requant_fn(cfg: LayerCfg, bits: int):
+    if cfg.bf16_state:
+        return po.round_state_bf16
     return lambda S: po.quantize_state(S, bits, cfg.group, cfg.asym)
 
 
@@ -406,6 +418,8 @@ def prefill_layer(cfg: LayerCfg, state: np.ndarray, q, k, v, a, beta, tiles=None
     """Oracle of pace_prefill_chunk.  q, k [B, T, Hk, dk]; v [B, T, Hv, dv]; a, beta
     [B, T, Hv].  Returns (o [B, T, Hv, dv], new state bytes, pre-rounding state of the
     last chunk {(b, h): S})."""
+    if cfg.bf16_state:
+        raise ValueError("prefill is defined for the packed states only")
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     a, beta = np.asarray(a, dtype=np.float64), np.asarray(beta, dtype=np.float64)
     B, T = a.shape[0], a.shape[1]

@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "round_to_bf16", "bf16_bits", "from_bf16_bits",
-    "TokenInputs", "make_tokens", "random_packed_state_parts", "random_buffer_parts",
+    "TokenInputs", "make_tokens", "random_packed_state_parts", "random_buffer_parts", "random_bf16_state",
 ]
 
 
@@ -158,6 +158,13 @@ def random_packed_state_parts(seed: int, B: int, Hv: int, dk: int, dv: int, grou
             row.append((codes, scales, zeros))
         out.append(row)
     return out
+
+
+def random_bf16_state(seed: int, B: int, Hv: int, dk: int, dv: int, scale: float = 0.3):
+    """Seeded random bf16-representable state values [B, Hv, dk, dv] (float32), drawn
+    N(0, scale^2) and rounded to bf16: any such array is a legal bf16 state."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return round_to_bf16((rng.standard_normal((B, Hv, dk, dv)) * scale).astype(np.float32))
 
 
 def random_buffer_parts(seed: int, B: int, Hv: int, Hk: int, dk: int, dv: int, dP: int,

@@ -144,6 +144,34 @@ int main() {
     bad = c; bad.Hk = 3;
     EXPECT(pace_prefill_workspace_bytes(&bad, 10, &ws) == PACE_EINVAL && ws == 5, "bad cfg");
   }
+  // ------------------------------------------------------------ bf16 state
+  {
+    pace_layer_cfg c = cfg_of(64, 32, 16, 128, 64, PACE_STATE_BF16, PACE_BUF_INT8, PACE_IO_BF16, 8, nullptr);
+    pace_layout_info info;
+    EXPECT(pace_layout(&c, &info) == PACE_OK, "bf16 state layout");
+    EXPECT(info.seq_stride == 32u * 128 * 128 * 2 && info.state_bytes == 64u * info.seq_stride, "bf16 state bytes");
+    EXPECT(info.payload_bits == 16.0, "bf16 payload");
+    c.group = 0;                                   // ignored for a bf16 state
+    EXPECT(pace_layout(&c, &info) == PACE_OK, "bf16 state ignores the group");
+    void *st = fake(0x100000), *bu = fake(0x200000), *io = fake(0x300000);
+    const float* f = (const float*)fake(0x400000);
+    EXPECT(pace_decode_step(&c, st, bu, io, io, io, f, f, nullptr, io, nullptr) == PACE_OK, "bf16 state decode");
+    EXPECT(last_decode.bf16_state == 1 && last_decode.rec4 == 128u * 128 * 2 && last_decode.mask8 == 0,
+           "bf16 state launch parameters");
+    EXPECT(pace_prefill_chunk(&c, st, io, io, io, f, f, 256, io, nullptr, 0, nullptr) == PACE_EUNSUPPORTED,
+           "bf16 state prefill");
+    int32_t ord[64];
+    for (int i = 0; i < 64; ++i) ord[i] = i;
+    EXPECT(pace_decode_step_ordered(&c, st, bu, io, io, io, f, f, nullptr, ord, io, nullptr) == PACE_EUNSUPPORTED,
+           "bf16 state ordered");
+    c.buf_kind = PACE_BUF_K4_VBF16;
+    EXPECT(pace_layout(&c, &info) == PACE_EUNSUPPORTED, "bf16 state with the mixed buffer");
+    int8_t hb[32] = {};
+    for (int h = 0; h < 32; ++h) hb[h] = 4;
+    c.buf_kind = PACE_BUF_INT8;
+    c.head_bits = hb;
+    EXPECT(pace_layout(&c, &info) == PACE_EINVAL, "bf16 state with a head map");
+  }
   // ------------------------------------------------------------ head allocation
   for (int trial = 0; trial < 200; ++trial) {
     const int H = 1 + (int)(rng() % 64), n8 = (int)(rng() % (H + 1)), dP = 1 + (int)(rng() % 32);

@@ -125,3 +125,31 @@ def check_flushed_tiles(pre: dict, q_gpu_tiles, label=""):
         total += n
     assert total_flips <= 1e-4 * total + 1, f"{label} {total_flips} code flips in {total} entries"
     return total_flips, total
+
+
+def _bf16_neighbour(w: float, up: bool) -> float:
+    """The bf16 value next to w (a bf16 value) toward +inf (up) or -inf."""
+    nudge = max(abs(w) * 2.0 ** -20, 2.0 ** -140)
+    return float(po.bf16_ceil(w + nudge)) if up else -float(po.bf16_ceil(-w + nudge))
+
+
+def check_bf16_rounding(stored, x, tol, label=""):
+    """bf16 values a kernel stored after rounding its fp32 value of x (fp64 oracle values).
+
+    Each stored value must be bf16_rne of fp32(x), unless x lies within `tol` (the fp32
+    evaluation error bound of the element, same shape) of the edge of the stored value's
+    rounding interval: then the stored value must be the bf16 rounding of some value
+    within tol of x.  Returns the number of such deviations."""
+    stored = np.asarray(stored, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    tol = np.broadcast_to(np.asarray(tol, dtype=np.float64), x.shape)
+    want = po.bf16_rne(po.to_f32(x))
+    bad = np.nonzero(stored != want)
+    for idx in zip(*bad):
+        g, w, xv, t = float(stored[idx]), float(want[idx]), float(x[idx]), float(tol[idx])
+        assert float(po.bf16_rne(g)) == g, f"{label} stored {g!r} is not a bf16 value"
+        lo, hi = 0.5 * (g + _bf16_neighbour(g, False)), 0.5 * (g + _bf16_neighbour(g, True))
+        assert xv + t >= lo and xv - t <= hi, (
+            f"{label} at {idx}: stored {g!r} vs rne {w!r}; x = {xv!r} lies "
+            f"{min(abs(xv - lo), abs(xv - hi)):.3g} outside its rounding interval (error bound {t:.3g})")
+    return int(bad[0].size)

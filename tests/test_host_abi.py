@@ -198,3 +198,26 @@ def test_prefill_workspace_query_distinguishes_errors_from_zero():
     assert out.value == 12345
     with pytest.raises(pace.PaceError):
         pace.prefill_workspace_bytes(pace.LayerConfig(B=2, Hv=4, Hk=3, dk=64, dv=64, group=32), 256)
+
+
+def test_bf16_state_layout_matches_the_oracles():
+    """PACE_STATE_BF16: one dv x dk bf16 record per (sequence, head), 16 payload bits, no
+    head map, int8 buffer only; the sizes agree with the oracle's byte layout."""
+    pace = _pace()
+    for d, B, Hv, Hk in [(128, 64, 32, 16), (64, 3, 4, 2)]:
+        g = pace.LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, buf="int8", bf16_state=True)
+        o = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=64, asym=False, buf="int8", dP=8, bf16_state=True)
+        L = pace.layout(g)
+        offs, stride, total = pk.state_layout(o)
+        assert L["state_bytes"] == total and L["seq_stride"] == stride == Hv * d * d * 2
+        assert L["buffer_bytes"] == pk.buffer_layout(o)[1]
+        assert L["payload_bits"] == 16.0
+    with pytest.raises(pace.PaceError) as e:
+        pace.layout(pace.LayerConfig(B=2, Hv=4, Hk=2, dk=128, dv=128, group=64, buf="mixed", bf16_state=True))
+    assert e.value.status == pace.PACE_EUNSUPPORTED
+    with pytest.raises(pace.PaceError) as e:
+        pace.layout(pace.LayerConfig(B=2, Hv=4, Hk=2, dk=128, dv=128, group=64, bf16_state=True, head_bits=[4] * 4))
+    assert e.value.status == pace.PACE_EINVAL
+    with pytest.raises(pace.PaceError) as e:
+        pace.prefill_workspace_bytes(pace.bf16_periodic(B=2, Hv=4, Hk=2), 256)
+    assert e.value.status == pace.PACE_EUNSUPPORTED
