@@ -23,9 +23,14 @@ mean launch duration in the timed region (timed-region time / launches; the grap
 only decode launches).  traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE +
 WRITE_SIZE, scaled by the same counters on a copy of known size, read from the committed
 counter summary when it was taken on the current kernel source, else null.
-Also reported: a same-box copy ceiling, the bf16 per-token-state baseline on the same
-tokens, a batch sweep B = 1, 16, 32, 64, 128 (PACE-4 and bf16 at each), and
-cpu_baseline: the fp64 oracle on a bounded sample of the same workload on one host core.
+Also reported: same-box bounds for a launch of this shape (a no-op kernel and a read-only
+stream of the same bytes in the same grid, timed in the same graph arrangement), the bf16
+per-token-state baseline on the same tokens, PACE-4/8 with both buffers and the decode
+buffer on a bf16 state at the same batch (with the split of the gain over the per-token
+baseline into the buffer's share and the 4-bit state's share), a batch sweep
+B = 1, 16, 32, 64, 128 (PACE-4, bf16 per-token and bf16-state periodic at each), the long
+chunked prefill, and cpu_baseline: the fp64 oracle on a bounded sample of the same
+workload on one host core.
 """
 from __future__ import annotations
 
@@ -55,7 +60,12 @@ def parse():
     ap.add_argument("--dim", type=int, default=128)
     ap.add_argument("--dP", type=int, default=8)
     ap.add_argument("--context", type=int, default=512)
-    ap.add_argument("--variant", choices=["pace4", "pace48-int8", "pace48-mixed"], default="pace4")
+    ap.add_argument("--variant", choices=["pace4", "pace48-int8", "pace48-mixed", "bf16-periodic"], default="pace4")
+    ap.add_argument("--variants", action="store_true", default=True,
+                    help="also time PACE-4/8 (int8 and mixed buffers) and the bf16-state periodic decode")
+    ap.add_argument("--no-variants", dest="variants", action="store_false")
+    ap.add_argument("--ceilings", action="store_true", default=True)
+    ap.add_argument("--no-ceilings", dest="ceilings", action="store_false")
     ap.add_argument("--baseline", action="store_true", default=True)
     ap.add_argument("--no-baseline", dest="baseline", action="store_false")
     ap.add_argument("--cpu-baseline", action="store_true", default=True)
@@ -206,6 +216,49 @@ def copy_ceiling(torch, nbytes=1 << 30, reps=5):
     return gbs
 
 
+def measure_ceilings(torch, bytes_per_launch, gx, gy, layers, dP, steps, warmup, threads=128):
+    """Same-box bounds for one decode launch of this shape, timed exactly like the decode (a
+    graph of layers x dP launches on one stream, `warmup` untimed replays, then `steps`
+    timed ones):
+      empty  -- a kernel that does nothing, grid (gx, gy) x threads: the fixed cost of a
+                launch of this shape in a graph (dispatch, start-up, end of kernel);
+      stream -- a read-only non-temporal stream of the decode launch's byte count in the
+                same grid, each layer on its own buffer (so, like the decode's states, the
+                stream comes from HBM): the fastest a launch moving those bytes can be.
+    Kernels from libpace_measure.so (include/pace_measure.h)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "bit_recurrent_state_amd", "libpace_measure.so"))
+    lib.pace_measure_empty.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.pace_measure_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    wgs = gx * gy
+    bpw = -(-int(bytes_per_launch) // (wgs * 16)) * 16
+    bufs = [torch.zeros(bpw * wgs, dtype=torch.uint8, device="cuda") for _ in range(layers)]
+    sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def checked(fn, *a):
+        def call():
+            r = fn(*a)
+            if r != 0:
+                raise RuntimeError(f"{fn.__name__} returned {r}")
+        return call
+    empty = [checked(lib.pace_measure_empty, gx, gy, threads, sp) for _ in range(layers * dP)]
+    streams = [checked(lib.pace_measure_stream, ctypes.c_void_p(bufs[l].data_ptr()), bpw, gx, gy, threads,
+                       ctypes.c_void_p(sink.data_ptr()), sp) for _ in range(dP) for l in range(layers)]
+    ms_e = time_graph(torch, stream, empty, steps, warmup)
+    ms_s = time_graph(torch, stream, streams, steps, warmup)
+    n = layers * dP * steps
+    e_us, s_us = ms_e * 1e3 / n, ms_s * 1e3 / n
+    res = {"empty_launch_us": round(e_us, 3), "stream_launch_us": round(s_us, 3),
+           "stream_bytes_per_launch": bpw * wgs, "stream_GBps": round(bpw * wgs / (s_us * 1e-6) / 1e9, 1),
+           "shape": f"grid ({gx}, {gy}) x {threads} threads, {layers} buffers x {dP} launches per graph replay"}
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def head_map(torch, pace, args, layer):
     """PACE-4/8 head map of one layer: e_h, a_h from a seeded 512-token calibration run on
     the GPU (pace_calibrate_heads, asymmetric 4-bit quantiser with 32-key groups), then the
@@ -221,12 +274,15 @@ def head_map(torch, pace, args, layer):
     return [int(x) for x in bits]
 
 
-def make_cfgs(torch, pace, args, B):
+def make_cfgs(torch, pace, args, B, variant=None):
     """One layer configuration per layer (PACE-4/8 layers differ in their head maps)."""
     d, Hv, Hk, dP = args.dim, args.heads, args.kv_heads, args.dP
-    if args.variant == "pace4":
+    variant = variant or args.variant
+    if variant == "pace4":
         return [pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP)] * args.layers
-    buf = "int8" if args.variant == "pace48-int8" else "mixed"
+    if variant == "bf16-periodic":
+        return [pace.bf16_periodic(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP)] * args.layers
+    buf = "int8" if variant == "pace48-int8" else "mixed"
     return [pace.pace48(head_map(torch, pace, args, l), B=B, Hv=Hv, Hk=Hk, d=d, dP=dP, buf=buf)
             for l in range(args.layers)]
 
@@ -242,20 +298,28 @@ def build_layers(torch, pace, args, cfgs):
         st = torch.zeros(L["state_bytes"], dtype=torch.uint8, device="cuda")
         bu = torch.zeros(L["buffer_bytes"], dtype=torch.uint8, device="cuda")
         ctx = make_layer_inputs(torch, B, args.context + dP, Hv, Hk, d, 1000 * args.seed + l)
-        o_ctx = torch.empty((B, args.context, Hv, d), dtype=torch.bfloat16, device="cuda")
-        pq, pk_, pv, pa, pb = (x[:, :args.context].contiguous() for x in ctx)
-        ws_n = pace.prefill_workspace_bytes(cfg, args.context)
-        ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
-        pace.prefill_chunk(cfg, st, pq, pk_, pv, pa, pb, o_ctx, workspace=ws)
-        toks = [tuple(x[:, args.context + t].contiguous() for x in ctx) for t in range(dP)]
         o = torch.empty((B, Hv, d), dtype=torch.bfloat16, device="cuda")
+        if cfg.bf16_state:
+            # a bf16 state takes no prefill call: the context is written token by token by
+            # the per-token bf16 kernel, whose state layout it shares
+            sb = st.view(torch.bfloat16)
+            for t in range(args.context):
+                pace.bf16_decode_step(cfg, sb, *(x[:, t].contiguous() for x in ctx), o)
+        else:
+            o_ctx = torch.empty((B, args.context, Hv, d), dtype=torch.bfloat16, device="cuda")
+            pq, pk_, pv, pa, pb = (x[:, :args.context].contiguous() for x in ctx)
+            ws_n = pace.prefill_workspace_bytes(cfg, args.context)
+            ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
+            pace.prefill_chunk(cfg, st, pq, pk_, pv, pa, pb, o_ctx, workspace=ws)
+            del o_ctx, pq, pk_, pv, pa, pb, ws
+        toks = [tuple(x[:, args.context + t].contiguous() for x in ctx) for t in range(dP)]
         layers.append(dict(cfg=cfg, state=st, buf=bu, toks=toks, o=o))
-        del ctx, o_ctx, pq, pk_, pv, pa, pb, ws
+        del ctx
     torch.cuda.synchronize()
     return layers, L
 
 
-def run_decode(torch, pace, args, B, steps, warmup, split=False, phases=None, ordered=False):
+def run_decode(torch, pace, args, B, steps, warmup, split=False, phases=None, ordered=False, variant=None):
     """Decode periods of the L-layer stack at batch B.  Returns a dict of figures.
 
     phases: optional per-sequence buffer counts to start from (continuous batching:
@@ -266,7 +330,7 @@ def run_decode(torch, pace, args, B, steps, warmup, split=False, phases=None, or
     the sequences that flush at that step placed first (what a continuous-batching
     scheduler, which knows every sequence's position in its period, would pass)."""
     t0 = time.time()
-    cfgs = make_cfgs(torch, pace, args, B)
+    cfgs = make_cfgs(torch, pace, args, B, variant)
     cfg = cfgs[0]
     dP, Lyr = cfg.dP, args.layers
     layers, L = build_layers(torch, pace, args, cfgs)
@@ -434,9 +498,13 @@ def main():
 
     torch.cuda.set_device(0)
     B, Hv, Hk, d, dP, Lyr = args.batch, args.heads, args.kv_heads, args.dim, args.dP, args.layers
-    cfg0 = pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP) if args.variant == "pace4" else \
-        pace.pace48([8] * (Hv // 4) + [4] * (Hv - Hv // 4), B=B, Hv=Hv, Hk=Hk, d=d, dP=dP,
-                    buf="int8" if args.variant == "pace48-int8" else "mixed")
+    if args.variant == "pace4":
+        cfg0 = pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP)
+    elif args.variant == "bf16-periodic":
+        cfg0 = pace.bf16_periodic(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP)
+    else:
+        cfg0 = pace.pace48([8] * (Hv // 4) + [4] * (Hv - Hv // 4), B=B, Hv=Hv, Hk=Hk, d=d, dP=dP,
+                           buf="int8" if args.variant == "pace48-int8" else "mixed")
     L0 = pace.layout(cfg0)
     log(f"variant {args.variant} B={B} Hv={Hv} Hk={Hk} d={d} dP={dP} layers={Lyr} "
         f"state/layer {L0['state_bytes'] / 1e6:.1f} MB buffer/layer {L0['buffer_bytes'] / 1e6:.1f} MB")
@@ -447,7 +515,11 @@ def main():
         f"without flush, {r['eager_flush_us']:.2f} us with (setup {r['setup_s']:.1f}s)")
     cfg, layers = r["cfg"], r.pop("layers")
     ceiling = copy_ceiling(torch)
-    log(f"copy ceiling {ceiling:.0f} GB/s")
+    log(f"device copy (torch, 1 GiB) {ceiling:.0f} GB/s")
+    ceil = None
+    if args.ceilings:
+        ceil = measure_ceilings(torch, r["bytes_per_launch"], Hv, B, Lyr, dP, args.steps, args.warmup)
+        log(f"ceilings at this launch shape: {ceil}")
     traffic = decode_traffic(args.variant + f"_b{B}") if args.variant == "pace4" else None
 
     result = {
@@ -464,7 +536,8 @@ def main():
         "dtype": {"pace4": "int4 state / int8 buffer / bf16 io, fp32 + int32 accumulate",
                   "pace48-int8": "int4 + int8 (quarter of heads) state / int8 buffer / bf16 io, fp32 + int32 accumulate",
                   "pace48-mixed": "int4 + int8 (quarter of heads) state / 4-bit key + bf16 value buffer / bf16 io, "
-                                  "fp32 + int32 accumulate"}[args.variant],
+                                  "fp32 + int32 accumulate",
+                  "bf16-periodic": "bf16 state / int8 buffer / bf16 io, fp32 accumulate"}[args.variant],
         "data": "synthetic (seeded; column-outlier value channels)",
         "config": {"workload": f"{args.variant} decode, {Lyr} gated-delta layers x {Hv} value heads "
                                f"({Hk} key heads), d={d}, B={B}, dP={dP}, {args.context}-token context; "
@@ -478,15 +551,44 @@ def main():
                      "mean_launch_us": round(r["launch_us"], 3),
                      "eager_launch_us": {"no_flush": round(r["eager_noflush_us"], 3),
                                          "flush": round(r["eager_flush_us"], 3)},
-                     "copy_ceiling_GBps": round(ceiling, 1),
-                     "frac_of_copy_ceiling": round(r["achieved"] / ceiling, 4)},
+                     "device_copy_GBps": round(ceiling, 1)},
     }
+    if ceil is not None:
+        result["roofline"].update({
+            "stream_ceiling_GBps": ceil["stream_GBps"], "frac_of_stream_ceiling": round(r["achieved"] / ceil["stream_GBps"], 4),
+            "empty_launch_us": ceil["empty_launch_us"], "stream_launch_us": ceil["stream_launch_us"],
+            "ceiling_note": "stream: a read-only stream of the same bytes per launch in the decode's grid, timed in "
+                            "the same graph arrangement; empty: a no-op kernel of that grid (libpace_measure.so)"})
 
     # ---- bf16 per-token-state baseline on the same shape
     if args.baseline:
         result["bf16_baseline"] = run_bf16_baseline(torch, pace, args, cfg, layers)
     del layers
     torch.cuda.empty_cache()
+
+    # ---- the other decode layouts at the same batch: PACE-4/8 with both buffers (head maps
+    # from the GPU calibration) and the decode buffer on a bf16 state
+    if args.variants and args.variant == "pace4":
+        legs = {}
+        for v in ("pace48-int8", "pace48-mixed", "bf16-periodic"):
+            rv = run_decode(torch, pace, args, B, args.steps, args.warmup, variant=v)
+            legs[v] = {"tokens_per_s": round(rv["tokens_per_s"], 1), "ms_per_step": round(rv["ms_per_step"], 4),
+                       "mean_launch_us": round(rv["launch_us"], 3), "bytes_per_launch": round(rv["bytes_per_launch"]),
+                       "roofline": {"bound": "hbm", "achieved": round(rv["achieved"], 1), "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": round(rv["achieved"] / HBM_PEAK_GBS, 4)}}
+            log(f"{v}: {legs[v]}")
+            del rv["layers"]
+            torch.cuda.empty_cache()
+        result["variants"] = legs
+        if args.baseline:
+            bl, bp = result["bf16_baseline"]["value"], legs["bf16-periodic"]["tokens_per_s"]
+            result["gain_split"] = {
+                "note": "decode tokens/s at this batch: per-token bf16 state -> decode buffer on a bf16 state -> "
+                        "decode buffer on the PACE-4 state ([p1] 'Assumptions and limits' attributes most of the gain "
+                        "to the buffer)",
+                "bf16_per_token": bl, "bf16_periodic": bp, "pace4": round(r["tokens_per_s"], 1),
+                "buffer_share_x": round(bp / bl, 3), "int4_state_share_x": round(r["tokens_per_s"] / bp, 3),
+                "total_x": round(r["tokens_per_s"] / bl, 3)}
 
     # ---- continuous batching: the same stack with every sequence at its own point of
     # the period (seeded uniform phases), so each step flushes about 1/dP of the tiles
@@ -523,6 +625,12 @@ def main():
                 ent["speedup_vs_bf16"] = round(rs["tokens_per_s"] / bl["value"], 3)
             del rs["layers"]
             torch.cuda.empty_cache()
+            if args.variants and args.variant == "pace4":
+                rp = run_decode(torch, pace, args, Bs, max(3, args.steps // 2), args.warmup, variant="bf16-periodic")
+                ent["bf16_periodic_tokens_per_s"] = round(rp["tokens_per_s"], 1)
+                ent["bf16_periodic_GBps"] = round(rp["achieved"], 1)
+                del rp["layers"]
+                torch.cuda.empty_cache()
             log(f"sweep B={Bs}: {ent}")
             sweep.append(ent)
         result["batch_sweep"] = sweep

@@ -221,3 +221,25 @@ def test_bf16_state_layout_matches_the_oracles():
     with pytest.raises(pace.PaceError) as e:
         pace.prefill_workspace_bytes(pace.bf16_periodic(B=2, Hv=4, Hk=2), 256)
     assert e.value.status == pace.PACE_EUNSUPPORTED
+
+
+def test_measurement_library_exports_its_header():
+    """libpace_measure.so (the launch-floor and streaming-ceiling kernels bench.py times)
+    exports every function include/pace_measure.h declares, and refuses bad shapes on the
+    host (no launch happens for an invalid call)."""
+    path = os.path.join(ROOT, "bit_recurrent_state_amd", "libpace_measure.so")
+    _pace()                                   # torch's HIP runtime first (see the binding)
+    lib = ctypes.CDLL(path)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pace_measure.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(pace_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["pace_measure_empty", "pace_measure_stream"]
+    for n in names:
+        assert hasattr(lib, n)
+    lib.pace_measure_empty.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert lib.pace_measure_empty(0, 1, 128, None) == -1
+    assert lib.pace_measure_empty(1, 1, 100, None) == -1
+    lib.pace_measure_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.pace_measure_stream(None, 4096, 32, 64, 128, ctypes.c_void_p(0x1000), None) == -1
+    assert lib.pace_measure_stream(ctypes.c_void_p(0x1008), 4096, 32, 64, 128, ctypes.c_void_p(0x1000), None) == -1
+    assert lib.pace_measure_stream(ctypes.c_void_p(0x1000), 4100, 32, 64, 128, ctypes.c_void_p(0x1000), None) == -1
