@@ -82,6 +82,10 @@ def parse():
     ap.add_argument("--prefill-tokens", type=int, default=32768)
     ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--prefill-warmup", type=int, default=8)
+    # profile post-processing (no GPU work): summaries of rocprofv3 CSV output
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--profile-command", default=None, help="command line(s) recorded in the summary")
     return ap.parse_args()
 
 
@@ -487,8 +491,100 @@ def decode_traffic(cfg_name):
         return None
 
 
+# --------------------------------------------------------- profile summaries ----
+
+def _csv_rows(root, suffix):
+    """Rows (dicts) of every rocprofv3 CSV under `root` whose name ends with `suffix`."""
+    import csv
+    rows = []
+    for dp, _, files in os.walk(root):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                with open(os.path.join(dp, f), newline="") as fh:
+                    rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(name, n=96):
+    name = name.replace("(anonymous namespace)::", "")
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def summarize_trace(trace_dir, command):
+    """Per-kernel duration statistics (microseconds) of a rocprofv3 --kernel-trace run."""
+    rows = _csv_rows(trace_dir, "kernel_trace.csv")
+    by = {}
+    for r in rows:
+        grid = "x".join(str(r.get(f"Grid_Size_{a}", r.get("Grid_Size", "?"))) for a in "XY")
+        key = (r["Kernel_Name"], grid)
+        by.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"command: {command}", "",
+             f"{'kernel':98s} {'grid (threads)':>16s} {'calls':>7s} {'avg us':>9s} {'median':>9s} {'min':>9s} "
+             f"{'max':>9s} {'total ms':>9s}"]
+    for (name, grid), d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(d)
+        lines.append(f"{_short(name):98s} {grid:>16s} {len(a):7d} {a.mean():9.3f} {np.median(a):9.3f} "
+                     f"{a.min():9.3f} {a.max():9.3f} {a.sum() / 1e3:9.3f}")
+    return "\n".join(lines)
+
+
+def _counter_means(pmc_dir, counter):
+    """{kernel name: (mean, min, max, dispatches)} of one counter (KiB per dispatch)."""
+    rows = _csv_rows(pmc_dir, "counter_collection.csv")
+    by = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (float(np.mean(v)), float(np.min(v)), float(np.max(v)), len(v)) for k, v in by.items()}
+
+
+def summarize_traffic(fetch_dir, write_dir, kernel_substr, copy_bytes, algorithmic_bytes, source, commands):
+    """HBM traffic per dispatch of the kernels whose name contains `kernel_substr`, from a
+    FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch), each scaled by what the same
+    counter reads on the largest runtime device copy of the run (copy_bytes read and
+    written: the 1 GiB copy bench.py times)."""
+    import hashlib
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    # the device copy of the run (the runtime's copy kernel) that moved the most bytes
+    copy_f = max(((k, v) for k, v in fetch.items() if "copyBuffer" in k), key=lambda kv: kv[1][0])
+    copy_w = max(((k, v) for k, v in write.items() if "copyBuffer" in k), key=lambda kv: kv[1][0])
+    kib = copy_bytes / 1024
+    ff, fw = kib / copy_f[1][0], kib / copy_w[1][0]
+    dk_f = [v for k, v in fetch.items() if kernel_substr in k]
+    dk_w = [v for k, v in write.items() if kernel_substr in k]
+    n_f, n_w = sum(v[3] for v in dk_f), sum(v[3] for v in dk_w)
+    f_mean = sum(v[0] * v[3] for v in dk_f) / n_f
+    w_mean = sum(v[0] * v[3] for v in dk_w) / n_w
+    fb, wb = f_mean * 1024 * ff, w_mean * 1024 * fw
+    sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    return "\n".join([
+        f"command_fetch: {commands[0]}", f"command_write: {commands[1]}",
+        f"copy_fetch_KiB: {copy_f[1][0]:.1f}   ({_short(copy_f[0], 60)}: {kib:.0f} KiB read -> factor {ff:.4f})",
+        f"copy_write_KiB: {copy_w[1][0]:.1f}   ({kib:.0f} KiB written -> factor {fw:.4f})",
+        f"decode_fetch_KiB_raw: {f_mean:.1f} (min {min(v[1] for v in dk_f):.1f}, max {max(v[2] for v in dk_f):.1f}, "
+        f"{n_f} dispatches)",
+        f"decode_write_KiB_raw: {w_mean:.1f} (min {min(v[1] for v in dk_w):.1f}, max {max(v[2] for v in dk_w):.1f}, "
+        f"{n_w} dispatches)",
+        f"fetch_bytes_per_launch: {fb:.0f}", f"write_bytes_per_launch: {wb:.0f}",
+        f"traffic_bytes_per_launch: {fb + wb:.0f}", f"algorithmic_bytes_per_launch: {algorithmic_bytes:.0f}",
+        f"traffic_over_algorithmic: {(fb + wb) / algorithmic_bytes:.4f}",
+        f"kernel_source_sha256: {sha}"])
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        d, out = args.summarize_trace
+        open(out, "w").write(summarize_trace(d, args.profile_command or "") + "\n")
+        return
+    if args.summarize_traffic:
+        fd, wd, out = args.summarize_traffic
+        cmds = (args.profile_command or " | ").split(" | ")
+        txt = summarize_traffic(fd, wd, "decode_kernel", 1 << 30, 23489024,
+                                os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", "pace_decode.hip"), cmds)
+        open(out, "w").write(txt + "\n")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the PACE decode path here runs on a single MI355X "
               f"and has no multi-GPU mode (asked for --gpus {args.gpus}).", file=sys.stderr)
