@@ -84,7 +84,16 @@ def parse():
     ap.add_argument("--prefill-warmup", type=int, default=8)
     # profile post-processing (no GPU work): summaries of rocprofv3 CSV output
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
-    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_LOG", "OUT_PREFIX"),
+                    help="per decode layout: HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE run of "
+                         "bench.py, against the algorithmic bytes in that run's JSON line (BENCH_LOG); writes "
+                         "OUT_PREFIX<layout>_b<B>.txt")
+    ap.add_argument("--launch-profile", action="store_true",
+                    help="no timing: one layer of the configured layout, a prefilled context, then 2 x dP eager "
+                         "decode launches (every position of the period twice), for a per-dispatch counter run")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("PMC_DIR", "OUT"),
+                    help="per position of the period: SQ instruction counts per wave of the decode launches of a "
+                         "--launch-profile counter run")
     ap.add_argument("--profile-command", default=None, help="command line(s) recorded in the summary")
     return ap.parse_args()
 
@@ -539,37 +548,122 @@ def _counter_means(pmc_dir, counter):
     return {k: (float(np.mean(v)), float(np.min(v)), float(np.max(v)), len(v)) for k, v in by.items()}
 
 
-def summarize_traffic(fetch_dir, write_dir, kernel_substr, copy_bytes, algorithmic_bytes, source, commands):
-    """HBM traffic per dispatch of the kernels whose name contains `kernel_substr`, from a
-    FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch), each scaled by what the same
-    counter reads on the largest runtime device copy of the run (copy_bytes read and
-    written: the 1 GiB copy bench.py times)."""
+DECODE_LAYOUTS = {  # (buffer, head bits, bf16 state) of decode_kernel<D, TOK, BUF, HB, IO, GT, AS, NTS, ORD, BFS>
+    "pace4": ("0", "4", "false"), "pace48-int8": ("0", "0", "false"), "pace48-mixed": ("1", "0", "false"),
+    "bf16-periodic": ("0", "4", "true")}
+
+
+def decode_layout(kernel_name):
+    """The decode layout a decode_kernel instantiation serves (launch order only), or None."""
+    if "decode_kernel<" not in kernel_name:
+        return None
+    args = [a.strip() for a in kernel_name.split("decode_kernel<", 1)[1].split(">", 1)[0].split(",")]
+    if len(args) < 10 or args[8] != "false":
+        return None
+    for name, (buf, hb, bfs) in DECODE_LAYOUTS.items():
+        if (args[2], args[3], args[9]) == (buf, hb, bfs):
+            return name
+    return None
+
+
+def summarize_traffic(fetch_dir, write_dir, bench_log, copy_bytes, source, commands):
+    """HBM traffic per dispatch of each decode layout's kernel, from a FETCH_SIZE run and a
+    WRITE_SIZE run (KiB per dispatch), each scaled by what the same counter reads on the
+    largest runtime device copy of the run (copy_bytes read and written: the 1 GiB copy
+    bench.py times).  Returns {layout: summary text}."""
     import hashlib
     fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
-    # the device copy of the run (the runtime's copy kernel) that moved the most bytes
-    copy_f = max(((k, v) for k, v in fetch.items() if "copyBuffer" in k), key=lambda kv: kv[1][0])
-    copy_w = max(((k, v) for k, v in write.items() if "copyBuffer" in k), key=lambda kv: kv[1][0])
+    res = [json.loads(l) for l in open(bench_log) if l.startswith("{")][-1]
+    B = res["config"]["global_batch"]
+    algo = {"pace4": res["roofline"]["bytes_per_launch"]}
+    for v, leg in res.get("variants", {}).items():
+        algo[v] = leg["bytes_per_launch"]
+    # the dispatch of the runtime's copy kernel that moved the most bytes (the 1 GiB copy)
+    copy_f = max(((k, v) for k, v in fetch.items() if "copyBuffer" in k), key=lambda kv: kv[1][2])
+    copy_w = max(((k, v) for k, v in write.items() if "copyBuffer" in k), key=lambda kv: kv[1][2])
     kib = copy_bytes / 1024
-    ff, fw = kib / copy_f[1][0], kib / copy_w[1][0]
-    dk_f = [v for k, v in fetch.items() if kernel_substr in k]
-    dk_w = [v for k, v in write.items() if kernel_substr in k]
-    n_f, n_w = sum(v[3] for v in dk_f), sum(v[3] for v in dk_w)
-    f_mean = sum(v[0] * v[3] for v in dk_f) / n_f
-    w_mean = sum(v[0] * v[3] for v in dk_w) / n_w
-    fb, wb = f_mean * 1024 * ff, w_mean * 1024 * fw
+    ff, fw = kib / copy_f[1][2], kib / copy_w[1][2]
     sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
-    return "\n".join([
-        f"command_fetch: {commands[0]}", f"command_write: {commands[1]}",
-        f"copy_fetch_KiB: {copy_f[1][0]:.1f}   ({_short(copy_f[0], 60)}: {kib:.0f} KiB read -> factor {ff:.4f})",
-        f"copy_write_KiB: {copy_w[1][0]:.1f}   ({kib:.0f} KiB written -> factor {fw:.4f})",
-        f"decode_fetch_KiB_raw: {f_mean:.1f} (min {min(v[1] for v in dk_f):.1f}, max {max(v[2] for v in dk_f):.1f}, "
-        f"{n_f} dispatches)",
-        f"decode_write_KiB_raw: {w_mean:.1f} (min {min(v[1] for v in dk_w):.1f}, max {max(v[2] for v in dk_w):.1f}, "
-        f"{n_w} dispatches)",
-        f"fetch_bytes_per_launch: {fb:.0f}", f"write_bytes_per_launch: {wb:.0f}",
-        f"traffic_bytes_per_launch: {fb + wb:.0f}", f"algorithmic_bytes_per_launch: {algorithmic_bytes:.0f}",
-        f"traffic_over_algorithmic: {(fb + wb) / algorithmic_bytes:.4f}",
-        f"kernel_source_sha256: {sha}"])
+    out = {}
+    for layout, a_bytes in algo.items():
+        dk_f = [(k, v) for k, v in fetch.items() if decode_layout(k) == layout]
+        dk_w = [(k, v) for k, v in write.items() if decode_layout(k) == layout]
+        if not dk_f or not dk_w:
+            continue
+        n_f, n_w = sum(v[3] for _, v in dk_f), sum(v[3] for _, v in dk_w)
+        f_mean = sum(v[0] * v[3] for _, v in dk_f) / n_f
+        w_mean = sum(v[0] * v[3] for _, v in dk_w) / n_w
+        fb, wb = f_mean * 1024 * ff, w_mean * 1024 * fw
+        out[f"{layout}_b{B}"] = "\n".join([
+            f"layout: {layout}, B = {B}; kernel(s): " + "; ".join(sorted({_short(k, 120) for k, _ in dk_f})),
+            f"command_fetch: {commands[0]}", f"command_write: {commands[1]}",
+            f"copy_fetch_KiB: {copy_f[1][2]:.1f}   ({_short(copy_f[0], 60)}: {kib:.0f} KiB read -> factor {ff:.4f})",
+            f"copy_write_KiB: {copy_w[1][2]:.1f}   ({kib:.0f} KiB written -> factor {fw:.4f})",
+            f"decode_fetch_KiB_raw: {f_mean:.1f} (min {min(v[1] for _, v in dk_f):.1f}, "
+            f"max {max(v[2] for _, v in dk_f):.1f}, {n_f} dispatches)",
+            f"decode_write_KiB_raw: {w_mean:.1f} (min {min(v[1] for _, v in dk_w):.1f}, "
+            f"max {max(v[2] for _, v in dk_w):.1f}, {n_w} dispatches)",
+            f"fetch_bytes_per_launch: {fb:.0f}", f"write_bytes_per_launch: {wb:.0f}",
+            f"traffic_bytes_per_launch: {fb + wb:.0f}", f"algorithmic_bytes_per_launch: {a_bytes:.0f}",
+            f"traffic_over_algorithmic: {(fb + wb) / a_bytes:.4f}",
+            f"kernel_source_sha256: {sha}"])
+    return out
+
+
+SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU",
+               "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY")
+
+
+def summarize_sq(pmc_dir, dP, command):
+    """Per position of the decode period (count before the step; the last one flushes):
+    mean SQ counts per wave over the decode_kernel dispatches of a --launch-profile run,
+    taken in dispatch order (dispatch i sits at position i mod dP)."""
+    rows = _csv_rows(pmc_dir, "counter_collection.csv")
+    by = {}
+    for r in rows:
+        if "decode_kernel" not in r["Kernel_Name"]:
+            continue
+        d = by.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    names = [c for c in SQ_COUNTERS if any(c in d for d in by.values())]
+    pos = {}
+    for i, k in enumerate(sorted(by)):
+        d = by[k]
+        w = d.get("SQ_WAVES", 0.0)
+        if w > 0:
+            pos.setdefault(i % dP, []).append([d.get(c, 0.0) / w for c in names])
+    lines = [f"command: {command}", "",
+             "per wave, mean over the dispatches at each position of the period (position dP - 1 flushes)",
+             f"{'position':>8s} " + " ".join(f"{c:>20s}" for c in names)]
+    for t in sorted(pos):
+        m = np.mean(np.array(pos[t]), axis=0)
+        lines.append(f"{t:8d} " + " ".join(f"{x:20.1f}" for x in m))
+    return "\n".join(lines)
+
+
+def launch_profile(torch, pace, args):
+    """One layer of the configured layout at batch args.batch: the context written by
+    pace_prefill_chunk, then 2 x dP eager decode launches (no timing)."""
+    cfg = make_cfgs(torch, pace, args, args.batch, None)[0]
+    B, Hv, Hk, d, dP = cfg.B, cfg.Hv, cfg.Hk, cfg.dk, cfg.dP
+    L = pace.layout(cfg)
+    st = torch.zeros(L["state_bytes"], dtype=torch.uint8, device="cuda")
+    bu = torch.zeros(L["buffer_bytes"], dtype=torch.uint8, device="cuda")
+    x = make_layer_inputs(torch, B, args.context + 2 * dP, Hv, Hk, d, 1000 * args.seed)
+    o = torch.empty((B, Hv, d), dtype=torch.bfloat16, device="cuda")
+    if cfg.bf16_state:           # (no prefill call for a bf16 state: the per-token kernel writes it)
+        for t in range(args.context):
+            pace.bf16_decode_step(cfg, st.view(torch.bfloat16), *(y[:, t].contiguous() for y in x), o)
+    else:
+        o_ctx = torch.empty((B, args.context, Hv, d), dtype=torch.bfloat16, device="cuda")
+        pace.prefill_chunk(cfg, st, *(t[:, :args.context].contiguous() for t in x), o_ctx)
+        del o_ctx
+    toks = [tuple(t[:, args.context + i].contiguous() for t in x) for i in range(2 * dP)]
+    torch.cuda.synchronize()
+    for tk in toks:
+        pace.decode_step(cfg, st, bu, *tk, o)
+    torch.cuda.synchronize()
+    log(f"launch profile: {2 * dP} decode launches of one {args.variant} layer at B={B}")
 
 
 def main():
@@ -579,11 +673,16 @@ def main():
         open(out, "w").write(summarize_trace(d, args.profile_command or "") + "\n")
         return
     if args.summarize_traffic:
-        fd, wd, out = args.summarize_traffic
+        fd, wd, blog, prefix = args.summarize_traffic
         cmds = (args.profile_command or " | ").split(" | ")
-        txt = summarize_traffic(fd, wd, "decode_kernel", 1 << 30, 23489024,
+        txt = summarize_traffic(fd, wd, blog, 1 << 30,
                                 os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", "pace_decode.hip"), cmds)
-        open(out, "w").write(txt + "\n")
+        for name, body in txt.items():
+            open(f"{prefix}{name}.txt", "w").write(body + "\n")
+        return
+    if args.summarize_sq:
+        d, out = args.summarize_sq
+        open(out, "w").write(summarize_sq(d, args.dP, args.profile_command or "") + "\n")
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the PACE decode path here runs on a single MI355X "
@@ -593,6 +692,9 @@ def main():
     import bit_recurrent_state_amd as pace
 
     torch.cuda.set_device(0)
+    if args.launch_profile:
+        launch_profile(torch, pace, args)
+        return
     B, Hv, Hk, d, dP, Lyr = args.batch, args.heads, args.kv_heads, args.dim, args.dP, args.layers
     if args.variant == "pace4":
         cfg0 = pace.pace4(B=B, Hv=Hv, Hk=Hk, d=d, dP=dP)
@@ -616,7 +718,7 @@ def main():
     if args.ceilings:
         ceil = measure_ceilings(torch, r["bytes_per_launch"], Hv, B, Lyr, dP, args.steps, args.warmup)
         log(f"ceilings at this launch shape: {ceil}")
-    traffic = decode_traffic(args.variant + f"_b{B}") if args.variant == "pace4" else None
+    traffic = decode_traffic(args.variant + f"_b{B}")
 
     result = {
         "metric": "decode tokens/s & achieved HBM GB/s (% peak), int4 state dP=8, B=1..128",
@@ -672,6 +774,8 @@ def main():
                        "mean_launch_us": round(rv["launch_us"], 3), "bytes_per_launch": round(rv["bytes_per_launch"]),
                        "roofline": {"bound": "hbm", "achieved": round(rv["achieved"], 1), "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": round(rv["achieved"] / HBM_PEAK_GBS, 4)}}
+            tv = decode_traffic(v + f"_b{B}")
+            legs[v]["roofline"]["traffic"] = None if tv is None else round(tv)
             log(f"{v}: {legs[v]}")
             del rv["layers"]
             torch.cuda.empty_cache()

@@ -149,6 +149,8 @@ FULL = {
     # name: (B, Hv, Hk, d, group, asym, buf, head_bits) -- the benchmark's layer shapes
     "pace4_b64": (64, 32, 16, 128, 64, False, "int8", None),
     "pace4_b128": (128, 32, 16, 128, 64, False, "int8", None),
+    # more tiles than one round of resident workgroups (eight per CU): a ragged second round
+    "pace4_b65_asym_g32": (65, 32, 16, 128, 32, True, "int8", None),
     "pace48_int8_b64": (64, 32, 16, 128, 32, True, "int8", "quarter"),
     "pace48_mixed_b64": (64, 32, 16, 128, 32, True, "mixed", "quarter"),
 }
@@ -171,8 +173,16 @@ def test_ordered_decode_full_size_sampled(name):
     full_size_case(name, ordered=True)
 
 
-def full_size_case(name, ordered):
-    print(f"[decode full size] case={name} ordered={ordered}", flush=True)
+def test_decode_full_size_two_rounds_with_inactive_sequences():
+    """B = 128 (4096 tiles: two rounds of resident workgroups) with an active mask that idles
+    sequences in both rounds."""
+    active = np.ones(128, dtype=np.uint8)
+    active[[0, 3, 64 + 1, 64 + 3, 10, 74]] = 0
+    full_size_case("pace4_b128", ordered=False, active=active)
+
+
+def full_size_case(name, ordered, active=None):
+    print(f"[decode full size] case={name} ordered={ordered} active_mask={active is not None}", flush=True)
     B, Hv, Hk, d, g, asym, buf, hb = FULL[name]
     if hb == "quarter":
         hb = [8 if h % 4 == 1 else 4 for h in range(Hv)]
@@ -188,15 +198,23 @@ def full_size_case(name, ordered):
     counts[::5] = dP - 1                               # a fifth of the sequences flush
     buffer = pk.pack_buffer(ocfg, random_buffer_parts(seed + 1, B, Hv, Hk, d, d, dP, buf == "mixed", counts=counts))
     toks = make_tokens(seed + 2, B, 1, Hv, Hk, d, d, bf16=True)
-    seqs = [0, 1, 2, B // 2, B // 2 + 3, B - 1]
+    seqs = [0, 1, 2, B // 2, B // 2 + 1, B // 2 + 3, B - 1]
+    if active is not None:
+        # (every fifth sequence flushes: 5, 70 and 75 flush in active tiles)
+        seqs = sorted(set(seqs) | {1, 2, 3, 4, 5, 64, 65, 66, 67, 68, 69, 70, 75})
     tiles = [(b, h) for b in seqs for h in (0, 1, 14, 15, Hv - 2, Hv - 1)]
-    o_ref, s_ref, b_ref, pre = pk.decode_step_layer(ocfg, state, buffer, *toks.token(0), tiles=tiles)
+    o_ref, s_ref, b_ref, pre = pk.decode_step_layer(ocfg, state, buffer, *toks.token(0), tiles=tiles,
+                                                    active=active)
     order = None
     if ordered:
         flushing = np.asarray(counts) == dP - 1
         order = np.concatenate([np.flatnonzero(flushing), np.flatnonzero(~flushing)])
-    o_gpu, s_gpu, b_gpu = run_gpu_decode(gcfg, state, buffer, toks, order=order)
-    parity.check_outputs(o_gpu, o_ref, tiles, name, out_bf16=True)
+    o_gpu, s_gpu, b_gpu = run_gpu_decode(gcfg, state, buffer, toks, order=order, active=active)
+    live = [(b, h) for b, h in tiles if active is None or active[b]]
+    parity.check_outputs(o_gpu, o_ref, live, name, out_bf16=True)
+    if active is not None:
+        for b in np.flatnonzero(np.asarray(active) == 0):
+            assert np.isnan(o_gpu[b]).all(), f"inactive output written (b={b})"
     assert len(pre) > 0
     qg = pk.unpack_state(ocfg, s_gpu, list(pre.keys()))
     parity.check_flushed_tiles(pre, qg, name)
@@ -216,7 +234,51 @@ def full_size_case(name, ordered):
             assert np.array_equal(dg["v"][b, h, :n], dr["v"][b, h, :n]), "bf16 v"
     old = np.repeat(np.asarray(counts)[:, None], Hv, axis=1)
     want = np.where(old + 1 >= dP, 0, old + 1)
+    if active is not None:
+        want = np.where(np.asarray(active)[:, None] != 0, want, old)
+        offs, stride, _ = pk.state_layout(ocfg)
+        n = pk.record_parts(ocfg, 4)[3]
+        for b in np.flatnonzero(np.asarray(active) == 0):
+            for h in range(Hv):
+                o = b * stride + offs[h]
+                assert np.array_equal(s_gpu[o:o + n], state[o:o + n]), f"inactive state changed (b={b},h={h})"
     assert np.array_equal(dg["count"], want), "count rule violated"
+
+
+def test_flush_full_size_b128():
+    """pace_flush_requant at B = 128 (two rounds of resident workgroups) under a sequence
+    mask, with sequences holding nothing to flush: every flushed tile matches the oracle,
+    every other state byte is untouched, the counts follow the mask."""
+    print("[flush full size] B=128 pace4", flush=True)
+    B, Hv, Hk, d, g, asym, buf, _ = FULL["pace4_b128"]
+    dP = 8
+    ocfg = pk.LayerCfg(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=g, asym=asym, buf=buf, dP=dP, bf16_io=True)
+    gcfg = _lib().LayerConfig(B=B, Hv=Hv, Hk=Hk, dk=d, dv=d, group=g, asym=asym, buf=buf, bf16_io=True, dP=dP)
+    seed = 911
+    state = pk.pack_state(ocfg, pk.state_from_parts(ocfg, random_packed_state_parts(seed, B, Hv, d, d, g,
+                                                                                     [4] * Hv, asym)))
+    counts = np.random.default_rng(seed + 7).integers(1, dP, size=B)
+    counts[[0, 64, 5, 70, 71]] = 0                    # nothing buffered
+    buffer = pk.pack_buffer(ocfg, random_buffer_parts(seed + 1, B, Hv, Hk, d, d, dP, False, counts=counts))
+    mask = np.array([0 if b % 7 == 3 else 1 for b in range(B)], dtype=np.uint8)
+    seqs = [0, 1, 2, 3, 4, 5, 6, 64, 65, 66, 67, 69, 70, 127]
+    tiles = [(b, h) for b in seqs for h in (0, 1, 14, 15, Hv - 1)]
+    s_ref, b_ref, pre = pk.flush_layer(ocfg, state, buffer, seq_mask=mask, tiles=tiles)
+    pace = _lib()
+    st, bu = dev(state), dev(buffer)
+    pace.flush_requant(gcfg, st, bu, seq_mask=dev(mask))
+    torch.cuda.synchronize()
+    s_gpu, b_gpu = st.cpu().numpy(), bu.cpu().numpy()
+    assert len(pre) > 0
+    check_states(ocfg, s_gpu, state, pre, tiles, "flush b128")
+    want = np.where((mask[:, None] != 0), 0, np.repeat(counts[:, None], Hv, axis=1))
+    assert np.array_equal(pk.unpack_buffer(ocfg, b_gpu)["count"], want), "flush count rule violated"
+    _, stride, _ = pk.state_layout(ocfg)
+    for b in range(B):
+        if mask[b] and counts[b] > 0:
+            continue
+        assert np.array_equal(s_gpu[b * stride:(b + 1) * stride], state[b * stride:(b + 1) * stride]), \
+            f"state of a sequence with nothing to flush changed (b={b})"
 
 
 def test_decode_inactive_sequences_untouched():
