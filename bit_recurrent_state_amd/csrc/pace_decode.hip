@@ -935,9 +935,9 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float y0 = fmaf(acc[2 * kb][i], rg[g], cr.magic), y1 = fmaf(acc[2 * kb + 1][i], rg[g], cr.magic);
-          if (asym) {
-            y0 = fminf(fmaxf(y0, cr.lo), cr.hi);
-            y1 = fminf(fmaxf(y1, cr.lo), cr.hi);
+          if (asym) {                         // clamp (lo <= hi): one median-of-three each
+            y0 = __builtin_amdgcn_fmed3f(y0, cr.lo, cr.hi);
+            y1 = __builtin_amdgcn_fmed3f(y1, cr.lo, cr.hi);
           }
           f0[i] = f32_bits(y0);
           f1[i] = f32_bits(y1);
