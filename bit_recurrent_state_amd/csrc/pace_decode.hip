@@ -849,16 +849,14 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
     // reduced over the four lanes (quarters) of the column; then each lane derives the
     // quantiser of one group (qq mod NG) and the others read it, rather than all four
     // lanes deriving every group.
-    float gmx[4], gmn[4];
+    float lmx[4], lmn[4];                   // this lane's range of each group
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      gmx[g] = 0.f;
-      gmn[g] = 0.f;
+      lmx[g] = 0.f;
+      lmn[g] = 0.f;
       if (g >= NG) break;
-      float mx, mn;
       if (asym) {
-        mx = -INFINITY;
-        mn = INFINITY;
+        float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           if (kb / kpg != g) continue;
@@ -868,29 +866,30 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
             mn = fminf(fminf(mn, acc[2 * kb][i]), acc[2 * kb + 1][i]);
           }
         }
-        mx = rows_max(mx);
-        mn = rows_min(mn);
+        lmx[g] = mx;
+        lmn[g] = mn;
       } else {                    // symmetric: only max |x| matters
-        mx = 0.f;
+        float mx = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           if (kb / kpg != g) continue;
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(fmaxf(mx, fabsf(acc[2 * kb][i])), fabsf(acc[2 * kb + 1][i]));
         }
-        mx = rows_max(mx);
-        mn = -mx;
+        lmx[g] = mx;
       }
-      gmx[g] = mx;
-      gmn[g] = mn;
     }
-    const int gm = qq & (NG - 1);           // this lane's group (NG is 1, 2 or 4)
-    float mxm = gmx[0], mnm = gmn[0];
-#pragma unroll
-    for (int g = 1; g < 4; ++g) {
-      mxm = g == gm ? gmx[g] : mxm;
-      mnm = g == gm ? gmn[g] : mnm;
-    }
+    // the range of this lane's group (row qq derives the quantiser of group qq mod NG),
+    // reduced over the four rows of the column
+    float mxm, mnm;
+    auto reduce_own = [&](auto ng) {
+      constexpr int G = decltype(ng)::value;
+      mxm = rows_reduce_own<G, true>(lmx);
+      mnm = asym ? rows_reduce_own<G, false>(lmn) : -mxm;
+    };
+    if (NG == 4) reduce_own(std::integral_constant<int, 4>{});
+    else if (NG == 2) reduce_own(std::integral_constant<int, 2>{});
+    else reduce_own(std::integral_constant<int, 1>{});
     const GroupQuant gq = group_quant(mnm, mxm, asym, bits);
     float rg[4];
     int zg[4];
