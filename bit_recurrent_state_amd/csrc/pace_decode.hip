@@ -404,7 +404,8 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
       } else {
         sm.v.b[n0][tid] = (uint16_t)pk_bf16(vx, 0.f);
       }
-      // q as three int8 pieces with power-of-two scales (q itself is not rounded)
+      // q as three int8 pieces with power-of-two scales: a split, not a rounding to a code
+      // grid; it reproduces each element exactly down to 2^-20 of max|q| (see int8_pieces)
       float q1, q2, q3;
       int e1;
       int8_pieces(qx, Mq, q1, q2, q3, e1);
