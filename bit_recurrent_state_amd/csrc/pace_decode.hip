@@ -159,8 +159,10 @@ __device__ inline void int8_pieces(float x, float M, float& p1, float& p2, float
 // Shared memory of one workgroup.  TOK = largest decode period this instantiation
 // serves; vector slots 0..TOK-1 are buffered tokens, TOK..TOK+2 the pieces of q.
 // Row strides are padded (codes: +16 bytes, projections: +4 floats) so that the 16 lanes
-// of an MFMA operand or output row group hit distinct LDS banks.
-template <int D, int TOK>
+// of an MFMA operand or output row group hit distinct LDS banks.  The value slots, the
+// scales and the zero points are sized for the instantiation's buffer kind, number of
+// scale groups (NGM) and symmetry (ZP: zero points present): 16.2 KB for PACE-4.
+template <int D, int TOK, int BUF, int NGM, bool ZP>
 struct alignas(16) Smem {
   static constexpr int NV = 16 * ((TOK + 3 + 15) / 16);
   static constexpr int CH = TOK / 8;        // 8-token chunks of the flush
@@ -169,7 +171,7 @@ struct alignas(16) Smem {
   alignas(16) int8_t kc[NV][KCS];           // B-operand codes of every slot
   alignas(16) union {
     int8_t c[TOK][D];                       // int8 buffer: value codes
-    uint16_t b[TOK][D];                     // mixed buffer: bf16 values
+    uint16_t b[BUF == PACE_BUF_K4_VBF16 ? TOK : 1][D];   // mixed buffer: bf16 values
   } v;
   alignas(16) union {
     float P[NV][PS];                        // projections
@@ -178,8 +180,8 @@ struct alignas(16) Smem {
   alignas(16) uint16_t kT[CH][D][8];        // key codes as bf16, rows in (tile, row) order
   alignas(16) float G[NV][NV];              // Gram matrix of the slots (scaled)
   float Gq[NV];                             // k_slot . q (the q pieces combined)
-  alignas(16) float scf[4][D];              // this tile's scales as fp32, [group][col]
-  alignas(16) uint8_t zeros[D][4];          // this tile's zero points, [col][group], a byte each
+  alignas(16) float scf[NGM][D];            // this tile's scales as fp32, [group][col]
+  alignas(16) uint8_t zeros[ZP ? D : 1][4]; // this tile's zero points, [col][group], a byte each
   float vscale[NV];                         // key scale of each token slot / q piece scale
   float vs[TOK], ga[TOK], gb[TOK];
   float red[3][4 * kWaves];                 // row maxima of |k|, |v|, |q|
@@ -207,7 +209,7 @@ template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS, boo
 // packed-state variants, so a 2048-tile launch runs in one round: at most 128 VGPRs.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!BFS && TOK <= 8 && GT != 0 ? 4 : 1)))
 void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
-  using SM = Smem<D, TOK>;
+  using SM = Smem<D, TOK, BUF, (GT != 0 ? D / GT : 4), AS != 0>;
   constexpr int NV = SM::NV;
   constexpr int NT = NV / 16;           // 16-vector MFMA column tiles
   constexpr int QS = TOK;               // first q-piece slot
@@ -397,7 +399,7 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
       sm.kc[n0][tid] = (int8_t)kcf;
       int8_t vcode = 0;
       float vs = 0.f;
-      if (BUF == PACE_BUF_INT8) {
+      if constexpr (BUF == PACE_BUF_INT8) {
         vs = div_rn(Mv, 127.f, 1.0f / 127.0f);
         vcode = (int8_t)(vs > 0.f ? fminf(fmaxf(rintf(vx / vs), -127.f), 127.f) : 0.f);
         sm.v.c[n0][tid] = vcode;
@@ -475,7 +477,7 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
       const int i = tid + it * kThreads;
       if (i < s0 * VV || i >= s1 * VV) continue;
       const uint4 vx4 = kLate ? vvl[it] : vv[it];
-      if (BUF == PACE_BUF_INT8) ((uint4*)&sm.v.c[0][0])[i] = vx4;
+      if constexpr (BUF == PACE_BUF_INT8) ((uint4*)&sm.v.c[0][0])[i] = vx4;
       else ((uint4*)&sm.v.b[0][0])[i] = vx4;
     }
   };
@@ -713,7 +715,9 @@ void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
         if (i >= n) continue;
       }
       const float ai = sm.ga[i];
-      const float vh = BUF == PACE_BUF_INT8 ? (float)sm.v.c[i][j] * sm.vs[i] : bf16_to_f32(sm.v.b[i][j]);
+      float vh;
+      if constexpr (BUF == PACE_BUF_INT8) vh = (float)sm.v.c[i][j] * sm.vs[i];
+      else vh = bf16_to_f32(sm.v.b[i][j]);
       const float ui = sm.gb[i] * (vh - ai * y[i]);
       u[i] = ui;
 #pragma unroll
