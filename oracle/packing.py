@@ -5,7 +5,7 @@ This is the oracle's own reading of the specification; it shares no code with th
 library's host or device side.  Only tests/, __graft_entry__.smoke() and bench.py's
 cpu_baseline leg may use it.
 
-Also holds the layer-level oracle drivers (decode step, flush, prefill) that work on
+Also holds the layer-level oracle routines (decode step, flush, prefill) that work on
 packed bytes, built from the per-tile functions of pace_oracle.
 """
 from __future__ import annotations
