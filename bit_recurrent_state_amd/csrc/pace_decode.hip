@@ -7,7 +7,7 @@
 // buffer is folded into the state, which is rounded once.
 //
 // One workgroup of 2 waves owns one (sequence, value head) tile, so all B x Hv tiles of
-// a layer are resident at once (8 workgroups per CU).  With S_0 the dequantised state,
+// a layer are resident at once at B = 64 and 32 heads (eight workgroups per CU).  With S_0 the dequantised state,
 // k^_i / v^_i the buffered (quantised) tokens and q the query:
 //   prologue     the current token, its gates, every buffer slot of the period and the
 //                tile's scales / zero points are requested at once (no address waits
@@ -15,7 +15,8 @@
 //                the token phase has used them, so the whole launch's token traffic is
 //                served ahead of the state stream.
 //   projections  p_i = S_0^T k^_i and r = S_0^T q on the int8 matrix cores: stored codes
-//                (A) times the buffer's key codes and three exact int8 pieces of q (B),
+//                (A) times the buffer's key codes and three int8 pieces of q (B; exact
+//                down to 2^-20 of max|q|),
 //                one 32-key block per MFMA so every MFMA lies inside one scale group;
 //                asymmetric zero points enter through a second MFMA per block (A = the
 //                column's zero point in every byte), so the accumulator is the exact
@@ -205,8 +206,9 @@ template <>
 struct OrderArg<false> {};
 
 template <int D, int TOK, int BUF, int HB, int IO, int GT, int AS, bool NTS, bool ORD = false, bool BFS = false>
-// Eight resident workgroups per CU (four waves per SIMD) for the specialised dP <= 8
-// packed-state variants, so a 2048-tile launch runs in one round: at most 128 VGPRs.
+// At least eight resident workgroups per CU (four waves per SIMD) for the specialised
+// dP <= 8 packed-state variants, so a 2048-tile launch runs in one round: at most 128
+// VGPRs (PACE-4 needs 86 and 16.2 KB of LDS, so ten fit).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!BFS && TOK <= 8 && GT != 0 ? 4 : 1)))
 void decode_kernel(DecodeParams p, OrderArg<ORD> ord) {
   using SM = Smem<D, TOK, BUF, (GT != 0 ? D / GT : 4), AS != 0>;
