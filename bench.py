@@ -817,6 +817,13 @@ def main():
             ent = {"B": Bs, "tokens_per_s": round(rs["tokens_per_s"], 1), "GBps": round(rs["achieved"], 1),
                    "mean_launch_us": round(rs["launch_us"], 3),
                    "working_set_MB": round((rs["L"]["state_bytes"] + rs["L"]["buffer_bytes"]) * Lyr / 1e6, 1)}
+            if args.ceilings and Bs > B:
+                # the same-box streaming ceiling and launch floor at this batch's launch shape
+                cb = measure_ceilings(torch, rs["bytes_per_launch"], Hv, Bs, Lyr, dP, max(3, args.steps // 2),
+                                      args.warmup)
+                ent.update({"stream_ceiling_GBps": cb["stream_GBps"], "stream_launch_us": cb["stream_launch_us"],
+                            "empty_launch_us": cb["empty_launch_us"],
+                            "frac_of_stream_ceiling": round(rs["achieved"] / cb["stream_GBps"], 4)})
             if args.baseline:
                 bl = run_bf16_baseline(torch, pace, args, rs["cfg"], rs["layers"], steps=max(3, args.steps // 2),
                                        warmup=args.warmup, split=False)
