@@ -12,23 +12,27 @@ typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
 __global__ void empty_kernel() {}
 
 // Each workgroup streams its own contiguous slice; lanes take consecutive 16-byte vectors,
-// so every wave instruction reads one contiguous 1 KB span.  Eight loads are in flight per
-// lane before the first is consumed.
+// so every wave instruction reads one contiguous 1 KB span.  A lane requests up to eight
+// vectors at once before consuming any (a slice of up to 8 x blockDim vectors is one round
+// of requests): out-of-range indices are clamped to the slice's last vector, which is
+// then not counted.
 __global__ void stream_kernel(const uint8_t* __restrict__ src, size_t bytes_per_wg, uint32_t* __restrict__ sink) {
   const unsigned w = blockIdx.y * gridDim.x + blockIdx.x;
   const v4u32* p = (const v4u32*)(src + (size_t)w * bytes_per_wg);
   const size_t nvec = bytes_per_wg / 16;
   const size_t step = blockDim.x;
   v4u32 acc = {0u, 0u, 0u, 0u};
-  size_t i = threadIdx.x;
-  for (; i + 7 * step < nvec; i += 8 * step) {
+  for (size_t i0 = threadIdx.x; i0 < nvec; i0 += 8 * step) {
     v4u32 r[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) r[u] = __builtin_nontemporal_load(p + i + u * step);
+    for (int u = 0; u < 8; ++u) {
+      const size_t i = i0 + u * step;
+      r[u] = __builtin_nontemporal_load(p + (i < nvec ? i : nvec - 1));
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc ^= r[u];
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u * step < nvec) acc ^= r[u];
   }
-  for (; i < nvec; i += step) acc ^= __builtin_nontemporal_load(p + i);
   uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
   // fold the workgroup's lanes into one word (the loads must not be dead code)
   for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
