@@ -184,10 +184,12 @@ def kernel_durations(torch, stream, calls, periods=2):
     return np.array([[s.elapsed_time(e) for s, e in row] for row in ev])
 
 
-def time_graph(torch, stream, calls, steps, warmup):
+def time_graph(torch, stream, calls, steps, warmup, replay_ms=None):
     """Capture `calls` once in a HIP graph on `stream`; replay it `warmup` times untimed,
     then `steps` times between two events on that stream, with a device synchronisation
-    on both sides.  Returns the timed milliseconds."""
+    on both sides.  Returns the timed milliseconds.  With a list `replay_ms`, `steps`
+    further replays follow, each between its own pair of events, and their durations are
+    appended to it (for the median per replay; not part of the returned time)."""
     with torch.cuda.stream(stream):
         for c in calls:                      # warm the path once outside capture
             c()
@@ -207,6 +209,15 @@ def time_graph(torch, stream, calls, steps, warmup):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
+    if replay_ms is not None:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        with torch.cuda.stream(stream):
+            for e0, e1 in ev:
+                e0.record(stream)
+                graph.replay()
+                e1.record(stream)
+        torch.cuda.synchronize()
+        replay_ms.extend(e0.elapsed_time(e1) for e0, e1 in ev)
     del graph
     return ms
 
@@ -366,12 +377,13 @@ def run_decode(torch, pace, args, B, steps, warmup, split=False, phases=None, or
             q, k, v, a, b_ = ly["toks"][t]
             calls.append(pace.prepare_decode_step(ly["cfg"], ly["state"], ly["buf"], q, k, v, a, b_, ly["o"],
                                                   stream=stream, order=order))
-    ms = time_graph(torch, stream, calls, steps, warmup)
+    replays = []
+    ms = time_graph(torch, stream, calls, steps, warmup, replay_ms=replays)
     n_launch = len(calls) * steps
     launch_s = ms / 1e3 / n_launch                       # mean launch duration in the timed region
     per_pos = np.array([algorithmic_bytes_per_launch(cfg, t, L) for t in range(dP)])
     bytes_per_launch = float(per_pos.mean())
-    res = dict(cfg=cfg, L=L, B=B, ms=ms, ms_per_step=ms / steps,
+    res = dict(cfg=cfg, L=L, B=B, ms=ms, ms_per_step=ms / steps, ms_per_step_median=float(np.median(replays)),
                tokens_per_s=B * dP * steps / (ms / 1e3),
                bytes_per_launch=bytes_per_launch, launch_us=launch_s * 1e6,
                achieved=bytes_per_launch / launch_s / 1e9,
@@ -728,6 +740,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms_per_step"], 4),
+        "ms_per_step_median": round(r["ms_per_step_median"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
